@@ -1,0 +1,176 @@
+/*
+ * flashsampling.h -- C ABI of the MI355X (gfx950) FlashSampling library.
+ *
+ * FlashSampling draws one token per row from softmax(H W^T / T) without ever
+ * writing the [B, V] logits to HBM: the LM-head product is computed tile by
+ * tile on chip, Gumbel noise is added to every logit, each workgroup keeps one
+ * (value, index) maximizer per row for its vocabulary tile, and a small
+ * reduction over tiles gives the sample.  This is exact because argmax
+ * decomposes over any partition of the vocabulary, and adding i.i.d. standard
+ * Gumbel noise before an argmax draws exactly from the softmax.
+ *   [FlashSampling: Fast and Memory-Efficient Exact Sampling, arXiv 2603.15854,
+ *    abstract; readus.org FlashSampling summary, sections "Gumbel Max Trick"
+ *    and on the two-stage FMMS kernel]
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; they must
+ *     stay valid until the work enqueued on `stream` has completed.  The
+ *     library never frees or retains them.
+ *   - bf16 tensors are passed as uint16_t bit patterns (the upper half of an
+ *     IEEE binary32).  Matrices are row-major with an explicit row stride in
+ *     elements (ld*), which must be a multiple of 8; H and W must be 16-byte
+ *     aligned (the kernels use 128-bit loads).
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Calls validate their arguments synchronously, enqueue work and return
+ *     without waiting.  Faults inside kernels surface at the caller's next
+ *     synchronisation, as with any HIP launch.
+ *   - Return value: FS_OK or a negative FS_ERR_* code; fs_last_error() then
+ *     holds a message (thread-local).  On an error nothing is enqueued.
+ *   - A context owns its device workspace (tile winners, counters).  Calls on
+ *     one context must not overlap in time: use one context per stream.
+ *   - Noise is a pure function of (seed, step, row, vocab id), so results do
+ *     not depend on tiling, code path or how rows are split across calls
+ *     (up to fp32 summation order in the logits).
+ */
+#ifndef FLASHSAMPLING_H_
+#define FLASHSAMPLING_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FS_OK = 0,
+  FS_ERR_INVALID_ARG = -1, /* a pointer, size, stride or value is out of its documented range */
+  FS_ERR_UNSUPPORTED = -2, /* a combination this build does not implement */
+  FS_ERR_CAPACITY = -3,    /* a size exceeds what the context was created for */
+  FS_ERR_HIP = -4          /* the HIP runtime reported an error (message in fs_last_error) */
+};
+
+enum { FS_COMBINE_GUMBEL = 0, FS_COMBINE_MAX = 1 };
+
+/* Code path selection for the streaming kernels (testing and measurement). */
+enum { FS_PATH_AUTO = 0, FS_PATH_DOT = 1, FS_PATH_MFMA = 2 };
+
+typedef struct fs_ctx fs_ctx;
+
+/* Per-row summary of one vocabulary group (grouped / online variant).
+ *   lse  = log sum_{allowed v in group} exp(logit_v / T)    (-inf if none allowed)
+ *   pmax = max_{allowed v in group} (logit_v / T + g_v)      (-inf if none allowed)
+ *   arg  = global vocab id attaining pmax, lowest on ties     (-1 if none allowed)
+ * The group's log-sum-exp is its "captain"; a Gumbel draw over captains picks
+ * the group, which is exact by hierarchical factorization of the categorical.
+ *   [arXiv 2603.15854 abstract; readus.org summary, section "Group Gumbel Max"] */
+typedef struct {
+  float lse;
+  float pmax;
+  int32_t arg;
+} fs_group_summary_t;
+
+/* Create a context on `device` for calls with B <= max_B, V <= max_V and
+ * top_k <= max_top_k.  Allocates the device workspace once; no later call
+ * allocates device memory.  *out is set to NULL on failure. */
+int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k);
+
+/* Release a context and its workspace (NULL is ignored).  Work that used the
+ * context must have completed. */
+void fs_destroy(fs_ctx* ctx);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* fs_last_error(void);
+
+/* Number of vocabulary tiles (= workgroups) and the tile bounds used by
+ * fs_fmms_sample for these sizes.  bounds, if not NULL, receives n_tiles + 1
+ * ascending vocab ids: tile i covers [bounds[i], bounds[i+1]).  Tiles are
+ * contiguous and balanced in units of 16 vocab rows. */
+int fs_fmms_tiling(fs_ctx* ctx, int B, int d, int64_t V, int path, int64_t* n_tiles, int64_t* bounds);
+
+/* Fused LM-head matmul + sample (FMMS).
+ *   H [B, d] bf16, row stride ldh;  W [V, d] bf16, row stride ldw.
+ *   logit[b][v] = sum_k H[b][k] W[v][k]   (bf16 products, fp32 accumulation)
+ *   s = logit * (1/T); masked ids -> -inf; with top_k > 0 only the top_k
+ *   largest s of the row's allowed ids are kept (ties at the boundary by lower
+ *   id); p = s + g(seed, step, b, v); out_idx[b] = argmax_v p (lowest id on
+ *   ties; -1 if the row has no allowed id).
+ *   g is standard Gumbel noise: r = word (v & 3) of Philox4x32-10 with key
+ *   (lo32 seed, hi32 seed) and counter (v >> 2, b, lo32 step, hi32 step);
+ *   u = (r + 1) / (2^32 + 1); g = -log(-log u).
+ *   [readus.org summary, code guide: API (weights, hidden states, temperature,
+ *    seed), RNG (Philox keyed by seed and coordinates), floating point (the u
+ *    formula); section on Top-K and masking]
+ * mask: NULL, or [B, ldm] uint32 words with ldm >= ceil(V/32): bit (v & 31)
+ *       of word (v >> 5) of row b set means id v is allowed.
+ * temperature: finite and > 0.
+ * out_idx: [B] int32 device.
+ * tile_max, tile_arg: NULL, or [B, n_tiles] (n_tiles from fs_fmms_tiling)
+ *       receiving each tile's maximum perturbed score and its id (top_k == 0
+ *       only); for tests.
+ * path: FS_PATH_AUTO, or force the dot-product or MFMA streaming kernel.
+ * Requires 1 <= B <= max_B, 8 <= d, d % 8 == 0, 1 <= V <= max_V < 2^31. */
+int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                   int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                   const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* tile_max,
+                   int32_t* tile_arg, int path);
+
+/* Unfused comparison path: the same LM-head product written to HBM as fp32
+ * logits, then a separate sampling kernel reads them back and applies the
+ * same scaling, mask, top-k, noise and argmax.  Same arguments and result as
+ * fs_fmms_sample (identical ids when the same path computes the logits).
+ * logits_ws: [B, ldl] fp32 device buffer with ldl >= V, ldl % 4 == 0,
+ *       16-byte aligned; receives the unscaled logits. */
+int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                      int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                      const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* logits_ws,
+                      int64_t ldl, int path);
+
+/* Grouped / online variant: summary of one vocabulary group.
+ *   W_group [G, d] bf16 (row stride ldw) holds the LM-head rows of global vocab
+ *   ids [vocab_offset, vocab_offset + G); noise uses the global ids, so the
+ *   group's pmax/arg are exactly the flat sampler's restricted to the group.
+ *   mask: NULL or the full-vocabulary mask [B, ldm] (word (v >> 5) of global
+ *   id v); vocab_offset % 32 == 0.
+ *   out: [B] device summaries.  [arXiv 2603.15854 abstract: grouped variants
+ *   for online and tensor-parallel settings; readus.org summary, "Group Gumbel
+ *   Max": stream groups, keep each group's captain, discard the rest] */
+int fs_group_summary(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W_group,
+                     int64_t ldw, int B, int d, int64_t vocab_offset, int64_t G, float temperature,
+                     uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out,
+                     int path);
+
+/* Combine per-group summaries s [n_groups, B] (group-major) into one sample
+ * per row.
+ *   FS_COMBINE_GUMBEL: k* = argmax_k (lse_k + g'_k) with g'_k the Gumbel
+ *     transform of word 0 of Philox4x32-10(key = seed, counter = (0x40000000 | k,
+ *     b, lo32 step, hi32 step)); out = arg_{k*}.  Equal to flat sampling in
+ *     distribution (hierarchical factorization).
+ *   FS_COMBINE_MAX: k* = argmax_k pmax_k; out = arg_{k*}.  Equal to the flat
+ *     sample exactly.
+ *   Ties go to the lowest k; a row with no finite key gets -1.
+ * Requires 1 <= n_groups <= 4096 and 1 <= B. */
+int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int n_groups, int B, uint64_t seed,
+                     uint64_t step, int mode, int32_t* out_idx);
+
+/* Test exports. */
+
+/* r_out[i] (if not NULL) = Philox word driving vocab id v0 + i of row `row` at
+ * (seed, step); g_out[i] (if not NULL) = its fp32 Gumbel noise.  n >= 0,
+ * v0 >= 0, v0 + n <= 2^31. */
+int fs_debug_philox(fs_ctx* ctx, void* stream, uint64_t seed, uint64_t step, int row, int64_t v0, int64_t n,
+                    uint32_t* r_out, float* g_out);
+
+/* g_out[i] = fp32 Gumbel noise of the 32-bit word r0 + i (r0 + n <= 2^32). */
+int fs_debug_gumbel_bits(fs_ctx* ctx, void* stream, uint64_t r0, int64_t n, float* g_out);
+
+/* Exhaustive device scan of the noise transform over all 2^32 words.
+ * stats_out (device, 4 x uint64): [0] = count of non-finite values,
+ * [1] = count of words r where g(r) < g(r - 1), [2] = bits of the minimum as
+ * float in the low 32 bits, [3] = same for the maximum. */
+int fs_debug_gumbel_scan(fs_ctx* ctx, void* stream, uint64_t* stats_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHSAMPLING_H_ */

@@ -1,0 +1,223 @@
+"""Python binding of libflashsampling.so: the C entry points under the same names.
+
+Argument marshalling only.  Tensors are PyTorch tensors on the library's GPU
+(PyTorch supplies device memory and streams); every computation happens in the
+HIP kernels behind the C ABI declared in include/flashsampling.h.  If the
+library has not been built, importing this module raises: there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashsampling.so")
+
+FS_OK = 0
+FS_ERR_INVALID_ARG = -1
+FS_ERR_UNSUPPORTED = -2
+FS_ERR_CAPACITY = -3
+FS_ERR_HIP = -4
+
+FS_COMBINE_GUMBEL = 0
+FS_COMBINE_MAX = 1
+
+FS_PATH_AUTO = 0
+FS_PATH_DOT = 1
+FS_PATH_MFMA = 2
+
+# exported symbols and their C signatures
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_F = ctypes.c_float
+SIGNATURES = {
+    "fs_create": (_I, [ctypes.POINTER(_P), _I, _I, _I64, _I]),
+    "fs_destroy": (None, [_P]),
+    "fs_last_error": (ctypes.c_char_p, []),
+    "fs_fmms_tiling": (_I, [_P, _I, _I, _I64, _I, ctypes.POINTER(_I64), _P]),
+    "fs_fmms_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _P, _I]),
+    "fs_unfused_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _I64,
+                               _I]),
+    "fs_group_summary": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _F, _U64, _U64, _P, _I64, _P, _I]),
+    "fs_group_combine": (_I, [_P, _P, _P, _I, _I, _U64, _U64, _I, _P]),
+    "fs_debug_philox": (_I, [_P, _P, _U64, _U64, _I, _I64, _I64, _P, _P]),
+    "fs_debug_gumbel_bits": (_I, [_P, _P, _U64, _I64, _P]),
+    "fs_debug_gumbel_scan": (_I, [_P, _P, _P]),
+}
+
+
+class FSError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"flashsampling error {code}: {message}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(rc: int) -> None:
+    if rc != FS_OK:
+        raise FSError(rc, _lib.fs_last_error().decode())
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _matrix(t: torch.Tensor, name: str) -> tuple[int, int, int]:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _mask_args(mask):
+    if mask is None:
+        return None, 0
+    if mask.dtype not in (torch.int32, torch.uint32) or mask.dim() != 2 or mask.stride(1) != 1:
+        raise TypeError("mask must be a 2-D row-major int32/uint32 tensor of packed words")
+    return mask.data_ptr(), mask.stride(0)
+
+
+# --- context ---------------------------------------------------------------
+
+def fs_create(device: int = 0, max_B: int = 256, max_V: int = 262144, max_top_k: int = 64) -> int:
+    h = _P()
+    _check(_lib.fs_create(ctypes.byref(h), device, max_B, max_V, max_top_k))
+    return h.value
+
+
+def fs_destroy(ctx: int) -> None:
+    _lib.fs_destroy(ctx)
+
+
+def fs_last_error() -> str:
+    return _lib.fs_last_error().decode()
+
+
+def fs_fmms_tiling(ctx: int, B: int, d: int, V: int, path: int = FS_PATH_AUTO):
+    """(n_tiles, bounds) with bounds a list of n_tiles + 1 vocab ids."""
+    n = _I64()
+    _check(_lib.fs_fmms_tiling(ctx, B, d, V, path, ctypes.byref(n), None))
+    bounds = (_I64 * (n.value + 1))()
+    _check(_lib.fs_fmms_tiling(ctx, B, d, V, path, ctypes.byref(n), bounds))
+    return n.value, list(bounds)
+
+
+# --- sampling ---------------------------------------------------------------
+
+def fs_fmms_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+                   mask: torch.Tensor | None = None, top_k: int = 0, out: torch.Tensor | None = None,
+                   tile_max: torch.Tensor | None = None, tile_arg: torch.Tensor | None = None,
+                   path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=H.device)
+    mptr, ldm = _mask_args(mask)
+    _check(_lib.fs_fmms_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
+                               float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(), _dptr(tile_max),
+                               _dptr(tile_arg), path))
+    return out
+
+
+def fs_unfused_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+                      mask: torch.Tensor | None = None, top_k: int = 0, out: torch.Tensor | None = None,
+                      logits_ws: torch.Tensor | None = None, path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=H.device)
+    if logits_ws is None:
+        logits_ws = torch.empty((B, (V + 3) // 4 * 4), dtype=torch.float32, device=H.device)
+    if logits_ws.dtype != torch.float32 or logits_ws.dim() != 2 or logits_ws.stride(1) != 1:
+        raise TypeError("logits_ws must be a 2-D row-major float32 tensor")
+    mptr, ldm = _mask_args(mask)
+    _check(_lib.fs_unfused_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
+                                  float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(),
+                                  logits_ws.data_ptr(), logits_ws.stride(0), path))
+    return out
+
+
+def summary_views(s: torch.Tensor):
+    """(lse, pmax, arg) views of a [..., 3] int32 tensor holding fs_group_summary_t records."""
+    return s[..., 0].view(torch.float32), s[..., 1].view(torch.float32), s[..., 2]
+
+
+def fs_group_summary(ctx: int, H: torch.Tensor, W_group: torch.Tensor, vocab_offset: int, temperature: float,
+                     seed: int, step: int, mask: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Returns out: [B, 3] int32 records (lse f32, pmax f32, arg i32); see summary_views."""
+    B, d, ldh = _matrix(H, "H")
+    G, d2, ldw = _matrix(W_group, "W_group")
+    if d2 != d:
+        raise ValueError("H and W_group disagree on d")
+    if out is None:
+        out = torch.empty((B, 3), dtype=torch.int32, device=H.device)
+    mptr, ldm = _mask_args(mask)
+    _check(_lib.fs_group_summary(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W_group.data_ptr(), ldw, B, d,
+                                 vocab_offset, G, float(temperature), seed, step, mptr, ldm, out.data_ptr(), path))
+    return out
+
+
+def fs_group_combine(ctx: int, summaries: torch.Tensor, seed: int, step: int, mode: int = FS_COMBINE_GUMBEL,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """summaries: [n_groups, B, 3] int32 records (contiguous)."""
+    if summaries.dtype != torch.int32 or summaries.dim() != 3 or summaries.shape[2] != 3 or not summaries.is_contiguous():
+        raise TypeError("summaries must be a contiguous [n_groups, B, 3] int32 tensor")
+    n_groups, B, _ = summaries.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=summaries.device)
+    _check(_lib.fs_group_combine(ctx, _stream_ptr(stream), summaries.data_ptr(), n_groups, B, seed, step, mode,
+                                 out.data_ptr()))
+    return out
+
+
+# --- test exports -------------------------------------------------------------
+
+def fs_debug_philox(ctx: int, seed: int, step: int, row: int, v0: int, n: int, device="cuda", stream=None):
+    r = torch.empty(n, dtype=torch.int32, device=device)
+    g = torch.empty(n, dtype=torch.float32, device=device)
+    _check(_lib.fs_debug_philox(ctx, _stream_ptr(stream), seed, step, row, v0, n, r.data_ptr(), g.data_ptr()))
+    return r, g
+
+
+def fs_debug_gumbel_bits(ctx: int, r0: int, n: int, device="cuda", stream=None) -> torch.Tensor:
+    g = torch.empty(n, dtype=torch.float32, device=device)
+    _check(_lib.fs_debug_gumbel_bits(ctx, _stream_ptr(stream), r0, n, g.data_ptr()))
+    return g
+
+
+def fs_debug_gumbel_scan(ctx: int, device="cuda", stream=None) -> torch.Tensor:
+    stats = torch.zeros(4, dtype=torch.int64, device=device)
+    _check(_lib.fs_debug_gumbel_scan(ctx, _stream_ptr(stream), stats.data_ptr()))
+    return stats

@@ -1,0 +1,397 @@
+// fs_api.hip -- C ABI of the FlashSampling library: argument checks, the
+// per-context device workspace, kernel selection and launches.  Every entry
+// point validates synchronously, enqueues on the caller's stream and returns.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/flashsampling.h"
+#include "fs_kernels.h"
+
+struct fs_ctx {
+  int device;
+  int max_B;
+  int64_t max_V;
+  int max_top_k;
+  int n_cu;
+  int max_tiles;
+  // [max_B][max_tiles] per-tile winners (and log-sum-exp state), plus tickets
+  float* ws_val;
+  int32_t* ws_idx;
+  float* ws_m;
+  float* ws_s;
+  unsigned int* tickets;  // one per kernel family, zero between launches
+  void* base;
+};
+
+namespace {
+
+enum { TICKET_STREAM = 0, TICKET_SAMPLE = 1, N_TICKETS = 4 };
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Runs the call with ctx->device current and restores the caller's device.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) {
+      ok = false;
+      return;
+    }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : dflt;
+}
+
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB).
+int choose_config(int B, int path, fsk::StreamConfig& cfg) {
+  const int dot_max = env_int("FS_DOT_MAX_B", 4);
+  bool dot;
+  if (path == FS_PATH_DOT) {
+    if (B > fsk::kDotMaxB) return fail(FS_ERR_UNSUPPORTED, "dot-product path supports B <= %d (got %d)", fsk::kDotMaxB, B);
+    dot = true;
+  } else if (path == FS_PATH_MFMA) {
+    dot = false;
+  } else {
+    dot = B <= dot_max && B <= fsk::kDotMaxB;
+  }
+  cfg.dot = dot;
+  cfg.bd = dot ? pow2_at_least(B) : 0;
+  cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : 4);
+  cfg.mb = (!dot && env_int("FS_MFMA_MB", 1) == 2) ? 2 : 1;
+  cfg.lds_bytes = 0;
+  return FS_OK;
+}
+
+int64_t mask_words(int64_t V) { return (V + 31) / 32; }
+
+int n_tiles_for(const fs_ctx* ctx, int64_t V) {
+  const int64_t nmb = (V + 15) / 16;
+  return (int)(nmb < ctx->max_tiles ? nmb : ctx->max_tiles);
+}
+
+// Common checks of the operands of a streaming call.
+int check_operands(const fs_ctx* ctx, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw, int B, int d,
+                   int64_t V, float temperature, const uint32_t* mask, int64_t ldm, int64_t mask_V) {
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if (!H || !W) return fail(FS_ERR_INVALID_ARG, "H and W must be non-NULL device pointers");
+  if (B < 1 || B > ctx->max_B) return fail(B < 1 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY, "B=%d outside [1, max_B=%d]", B, ctx->max_B);
+  if (d < 8 || d % 8 != 0) return fail(FS_ERR_INVALID_ARG, "d=%d must be a positive multiple of 8", d);
+  if (ldh < d || ldh % 8 != 0) return fail(FS_ERR_INVALID_ARG, "ldh=%lld must be >= d and a multiple of 8", (long long)ldh);
+  if (ldw < d || ldw % 8 != 0) return fail(FS_ERR_INVALID_ARG, "ldw=%lld must be >= d and a multiple of 8", (long long)ldw);
+  if (!aligned16(H) || !aligned16(W)) return fail(FS_ERR_INVALID_ARG, "H and W must be 16-byte aligned");
+  if (V < 1) return fail(FS_ERR_INVALID_ARG, "V=%lld must be >= 1", (long long)V);
+  if (V > ctx->max_V) return fail(FS_ERR_CAPACITY, "V=%lld exceeds max_V=%lld", (long long)V, (long long)ctx->max_V);
+  if (!(std::isfinite(temperature) && temperature > 0.0f))
+    return fail(FS_ERR_INVALID_ARG, "temperature must be finite and > 0 (got %g)", (double)temperature);
+  if (mask && ldm < mask_words(mask_V))
+    return fail(FS_ERR_INVALID_ARG, "ldm=%lld must be >= ceil(V/32)=%lld", (long long)ldm, (long long)mask_words(mask_V));
+  return FS_OK;
+}
+
+// Fills the fields common to all streaming launches.
+void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int64_t ldh, const uint16_t* W,
+                 int64_t ldw, int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                 const uint32_t* mask, int64_t ldm) {
+  std::memset(&p, 0, sizeof p);
+  p.H = H;
+  p.ldh = ldh;
+  p.W = W;
+  p.ldw = ldw;
+  p.B = B;
+  p.d = d;
+  p.V = V;
+  p.inv_t = 1.0f / temperature;
+  p.seed_lo = (uint32_t)seed;
+  p.seed_hi = (uint32_t)(seed >> 32);
+  p.step_lo = (uint32_t)step;
+  p.step_hi = (uint32_t)(step >> 32);
+  p.mask = mask;
+  p.ldm = ldm;
+  p.n_tiles = n_tiles_for(ctx, V);
+  p.n_mblocks = (V + 15) / 16;
+  p.ws_val = ctx->ws_val;
+  p.ws_idx = ctx->ws_idx;
+  p.ws_m = ctx->ws_m;
+  p.ws_s = ctx->ws_s;
+  p.ticket = ctx->tickets + TICKET_STREAM;
+}
+
+// Launches the streaming kernel over the batch in chunks of at most
+// kMfmaMaxB rows (each chunk streams W once).  `per_chunk` adjusts the output
+// pointers of a chunk that starts at batch row r0.
+template <typename F>
+int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk) {
+  const int B = base.B;
+  for (int r0 = 0; r0 < B; r0 += fsk::kMfmaMaxB) {
+    const int Bc = (B - r0) < fsk::kMfmaMaxB ? (B - r0) : fsk::kMfmaMaxB;
+    fsk::StreamParams p = base;
+    p.B = Bc;
+    p.H = base.H + (int64_t)r0 * base.ldh;
+    p.row_offset = r0;
+    per_chunk(p, r0);
+    fsk::StreamConfig cfg;
+    int rc = choose_config(Bc, path, cfg);
+    if (rc != FS_OK) return rc;
+    if (!fsk::plan_stream(p, cfg))
+      return fail(FS_ERR_UNSUPPORTED, "shape B=%d d=%d does not fit the LDS budget", Bc, p.d);
+    hipError_t e = fsk::launch_stream(p, cfg, epi, stream);
+    if (e != hipSuccess) return hip_fail(e, "streaming kernel launch");
+  }
+  return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fs_last_error(void) { return g_error.c_str(); }
+
+int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k) {
+  if (!out) return fail(FS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (max_B < 1) return fail(FS_ERR_INVALID_ARG, "max_B=%d must be >= 1", max_B);
+  if (max_V < 1 || max_V >= ((int64_t)1 << 31)) return fail(FS_ERR_INVALID_ARG, "max_V must be in [1, 2^31)");
+  if (max_top_k < 0) return fail(FS_ERR_INVALID_ARG, "max_top_k must be >= 0");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev) return fail(FS_ERR_INVALID_ARG, "device %d outside [0, %d)", device, ndev);
+  DeviceGuard guard(device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", device);
+  fs_ctx* c = new fs_ctx();
+  std::memset(c, 0, sizeof *c);
+  c->device = device;
+  c->max_B = max_B;
+  c->max_V = max_V;
+  c->max_top_k = max_top_k;
+  e = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  c->max_tiles = c->n_cu;
+  const size_t n = (size_t)max_B * (size_t)c->max_tiles;
+  const size_t bytes = 4 * n * sizeof(float) + N_TICKETS * sizeof(unsigned int) + 256;
+  e = hipMalloc(&c->base, bytes);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "hipMalloc(workspace)");
+  }
+  char* b = (char*)c->base;
+  c->tickets = (unsigned int*)b;
+  b += 256;
+  c->ws_val = (float*)b;
+  c->ws_idx = (int32_t*)(c->ws_val + n);
+  c->ws_m = (float*)(c->ws_idx + n);
+  c->ws_s = c->ws_m + n;
+  e = hipMemset(c->base, 0, bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(c->base);
+    delete c;
+    return hip_fail(e, "hipMemset(workspace)");
+  }
+  *out = c;
+  return FS_OK;
+}
+
+void fs_destroy(fs_ctx* ctx) {
+  if (!ctx) return;
+  DeviceGuard guard(ctx->device);
+  if (ctx->base) (void)hipFree(ctx->base);
+  delete ctx;
+}
+
+int fs_fmms_tiling(fs_ctx* ctx, int B, int d, int64_t V, int path, int64_t* n_tiles, int64_t* bounds) {
+  (void)d;
+  (void)path;
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if (B < 1 || V < 1 || V > ctx->max_V) return fail(FS_ERR_INVALID_ARG, "B or V out of range");
+  const int nt = n_tiles_for(ctx, V);
+  const int64_t nmb = (V + 15) / 16;
+  if (n_tiles) *n_tiles = nt;
+  if (bounds) {
+    for (int i = 0; i <= nt; ++i) {
+      const int64_t r = 16 * ((int64_t)i * nmb / nt);
+      bounds[i] = r < V ? r : V;
+    }
+  }
+  return FS_OK;
+}
+
+int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw, int B,
+                   int d, int64_t V, float temperature, uint64_t seed, uint64_t step, const uint32_t* mask,
+                   int64_t ldm, int top_k, int32_t* out_idx, float* tile_max, int32_t* tile_arg, int path) {
+  int rc = check_operands(ctx, H, ldh, W, ldw, B, d, V, temperature, mask, ldm, V);
+  if (rc != FS_OK) return rc;
+  if (!out_idx) return fail(FS_ERR_INVALID_ARG, "out_idx is NULL");
+  if (top_k < 0 || top_k > ctx->max_top_k)
+    return fail(top_k < 0 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY, "top_k=%d outside [0, max_top_k=%d]", top_k, ctx->max_top_k);
+  if (top_k > 0) return fail(FS_ERR_UNSUPPORTED, "top_k > 0 is not implemented by this build");
+  if ((tile_max == nullptr) != (tile_arg == nullptr)) return fail(FS_ERR_INVALID_ARG, "tile_max and tile_arg go together");
+  if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  fsk::StreamParams p;
+  fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
+  const int nt = p.n_tiles;
+  return run_stream_chunks(p, path, fsk::EPI_FLAT, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
+    c.out_idx = out_idx + r0;
+    c.dbg_max = tile_max ? tile_max + (int64_t)r0 * nt : nullptr;
+    c.dbg_arg = tile_arg ? tile_arg + (int64_t)r0 * nt : nullptr;
+  });
+}
+
+int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                      int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                      const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* logits_ws, int64_t ldl,
+                      int path) {
+  int rc = check_operands(ctx, H, ldh, W, ldw, B, d, V, temperature, mask, ldm, V);
+  if (rc != FS_OK) return rc;
+  if (!out_idx) return fail(FS_ERR_INVALID_ARG, "out_idx is NULL");
+  if (!logits_ws || !aligned16(logits_ws)) return fail(FS_ERR_INVALID_ARG, "logits_ws must be a 16-byte aligned device pointer");
+  if (ldl < V || ldl % 4 != 0) return fail(FS_ERR_INVALID_ARG, "ldl=%lld must be >= V and a multiple of 4", (long long)ldl);
+  if (top_k < 0 || top_k > ctx->max_top_k)
+    return fail(top_k < 0 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY, "top_k=%d outside [0, max_top_k=%d]", top_k, ctx->max_top_k);
+  if (top_k > 0) return fail(FS_ERR_UNSUPPORTED, "top_k > 0 is not implemented by this build");
+  if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  hipStream_t s = (hipStream_t)stream;
+  fsk::StreamParams p;
+  fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
+  rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
+    c.logits = logits_ws + (int64_t)r0 * ldl;
+    c.ldl = ldl;
+  });
+  if (rc != FS_OK) return rc;
+  fsk::SampleParams q;
+  std::memset(&q, 0, sizeof q);
+  q.logits = logits_ws;
+  q.ldl = ldl;
+  q.B = B;
+  q.V = V;
+  q.inv_t = 1.0f / temperature;
+  q.seed_lo = (uint32_t)seed;
+  q.seed_hi = (uint32_t)(seed >> 32);
+  q.step_lo = (uint32_t)step;
+  q.step_hi = (uint32_t)(step >> 32);
+  q.mask = mask;
+  q.ldm = ldm;
+  q.n_tiles = n_tiles_for(ctx, V);
+  q.ws_val = ctx->ws_val;
+  q.ws_idx = ctx->ws_idx;
+  q.ticket = ctx->tickets + TICKET_SAMPLE;
+  q.out_idx = out_idx;
+  hipError_t e = fsk::launch_sample_logits(q, s);
+  if (e != hipSuccess) return hip_fail(e, "sampling kernel launch");
+  return FS_OK;
+}
+
+int fs_group_summary(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W_group,
+                     int64_t ldw, int B, int d, int64_t vocab_offset, int64_t G, float temperature, uint64_t seed,
+                     uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out, int path) {
+  if (vocab_offset < 0 || vocab_offset % 32 != 0)
+    return fail(FS_ERR_INVALID_ARG, "vocab_offset=%lld must be a non-negative multiple of 32", (long long)vocab_offset);
+  if (G >= 1 && vocab_offset + G >= ((int64_t)1 << 31))
+    return fail(FS_ERR_INVALID_ARG, "vocab_offset + G must be < 2^31");
+  int rc = check_operands(ctx, H, ldh, W_group, ldw, B, d, G, temperature, mask, ldm, vocab_offset + G);
+  if (rc != FS_OK) return rc;
+  if (!out) return fail(FS_ERR_INVALID_ARG, "out is NULL");
+  if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  fsk::StreamParams p;
+  fill_common(p, ctx, H, ldh, W_group, ldw, B, d, G, temperature, seed, step, mask, ldm);
+  p.vocab_offset = vocab_offset;
+  return run_stream_chunks(p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
+    c.out_sum = reinterpret_cast<fsk::GroupSummary*>(out + r0);
+  });
+}
+
+int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int n_groups, int B, uint64_t seed,
+                     uint64_t step, int mode, int32_t* out_idx) {
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if (!s || !out_idx) return fail(FS_ERR_INVALID_ARG, "s and out_idx must be non-NULL");
+  if (n_groups < 1 || n_groups > 4096) return fail(FS_ERR_INVALID_ARG, "n_groups=%d outside [1, 4096]", n_groups);
+  if (B < 1) return fail(FS_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (mode != FS_COMBINE_GUMBEL && mode != FS_COMBINE_MAX) return fail(FS_ERR_INVALID_ARG, "unknown mode %d", mode);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  hipError_t e = fsk::launch_group_combine(reinterpret_cast<const fsk::GroupSummary*>(s), n_groups, B, seed, step,
+                                           mode, out_idx, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return FS_OK;
+}
+
+int fs_debug_philox(fs_ctx* ctx, void* stream, uint64_t seed, uint64_t step, int row, int64_t v0, int64_t n,
+                    uint32_t* r_out, float* g_out) {
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if (n < 0 || v0 < 0 || v0 + n > ((int64_t)1 << 31) || row < 0)
+    return fail(FS_ERR_INVALID_ARG, "need n >= 0, v0 >= 0, v0 + n <= 2^31, row >= 0");
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  hipError_t e = fsk::launch_debug_philox(seed, step, (uint32_t)row, v0, n, r_out, g_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug kernel launch");
+  return FS_OK;
+}
+
+int fs_debug_gumbel_bits(fs_ctx* ctx, void* stream, uint64_t r0, int64_t n, float* g_out) {
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if (!g_out || n < 0 || r0 + (uint64_t)n > ((uint64_t)1 << 32))
+    return fail(FS_ERR_INVALID_ARG, "need g_out, n >= 0 and r0 + n <= 2^32");
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  hipError_t e = fsk::launch_debug_gumbel_bits(r0, n, g_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug kernel launch");
+  return FS_OK;
+}
+
+int fs_debug_gumbel_scan(fs_ctx* ctx, void* stream, uint64_t* stats_out) {
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if (!stats_out) return fail(FS_ERR_INVALID_ARG, "stats_out is NULL");
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  hipError_t e = fsk::launch_debug_gumbel_scan((unsigned long long*)stats_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug kernel launch");
+  return FS_OK;
+}
+
+}  // extern "C"

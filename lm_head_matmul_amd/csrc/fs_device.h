@@ -1,0 +1,136 @@
+// fs_device.h -- device-side building blocks of the FlashSampling kernels (gfx950).
+//
+// Noise: Philox4x32-10 keyed on (seed, step, row, vocab id) and the transform of
+// a 32-bit word r into standard Gumbel noise through u = (r+1)/(2^32+1),
+// g = -log(-log u).  [readus.org FlashSampling summary, code guide sections 2
+// (Philox keyed by master seed and coordinates) and 3 (the u formula, which keeps
+// u strictly inside (0, 1))]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64-bit multiplies and xors; the key advances by a Weyl step after each
+// round.  One call yields the four words of four consecutive vocab ids.
+// ---------------------------------------------------------------------------
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t k0, uint32_t k1, uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c0;
+    const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
+    const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)pb;
+    c3 = (uint32_t)pa;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  Philox4 out;
+  out.w[0] = c0;
+  out.w[1] = c1;
+  out.w[2] = c2;
+  out.w[3] = c3;
+  return out;
+}
+
+// Counter of vocab quad (gv >> 2) of row b at a step: (gv >> 2, b, step lo, step hi).
+struct NoiseKey {
+  uint32_t seed_lo, seed_hi, step_lo, step_hi;
+};
+
+__device__ __forceinline__ Philox4 noise_quad(const NoiseKey& k, uint32_t quad, uint32_t row) {
+  return philox4x32_10(k.seed_lo, k.seed_hi, quad, row, k.step_lo, k.step_hi);
+}
+
+// ---------------------------------------------------------------------------
+// Gumbel noise of one word.  With m = r + 1 (r < 2^31) or m = 2^32 - r
+// (r >= 2^31), t = m * 2^-32 lies in (0, 1/2] and is the smaller of u and 1-u
+// (the factor 2^32/(2^32+1) is below fp32 resolution).  E = -ln u is then
+// -ln t (lower half) or -ln(1 - t) (upper half); the latter uses its Taylor
+// series for t < 1/16 (remainder below t * 2^-35) so that E keeps full
+// relative precision as u -> 1, where the largest noise values come from.
+// Every word gives a finite value in [-3.0992, 22.181].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_ln(float x) {  // hardware log2, x normal and > 0
+  return __builtin_amdgcn_logf(x) * 0.693147180559945309f;
+}
+
+__device__ __forceinline__ float gumbel_from_bits(uint32_t r) {
+  const bool upper = r >= 0x80000000u;
+  const uint32_t m = upper ? (0u - r) : (r + 1u);
+  const float t = (float)m * 0x1p-32f;
+  // -ln(1 - t) / t = sum_{n>=1} t^(n-1) / n, eight terms
+  float poly = 0.125f;
+  poly = __builtin_fmaf(poly, t, 0.142857142857142857f);
+  poly = __builtin_fmaf(poly, t, 0.166666666666666667f);
+  poly = __builtin_fmaf(poly, t, 0.2f);
+  poly = __builtin_fmaf(poly, t, 0.25f);
+  poly = __builtin_fmaf(poly, t, 0.333333333333333333f);
+  poly = __builtin_fmaf(poly, t, 0.5f);
+  poly = __builtin_fmaf(poly, t, 1.0f);
+  const float larg = upper ? (1.0f - t) : t;
+  const float ln_arg = fast_ln(larg);
+  const float e = (upper && t < 0.0625f) ? t * poly : -ln_arg;
+  return -fast_ln(e);
+}
+
+// ---------------------------------------------------------------------------
+// (value, index) maximizer with the lowest-index tie rule.  NaN values never
+// win: they fail every comparison.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool beats(float va, int32_t ia, float vb, int32_t ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void merge_best(float& v, int32_t& i, float ov, int32_t oi) {
+  if (beats(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Online log-sum-exp state (running max m, sum of exp(x - m)).
+__device__ __forceinline__ void lse_push(float& m, float& s, float x) {
+  if (x == -INFINITY) return;
+  if (x > m) {
+    s = s * __expf(m - x) + 1.0f;
+    m = x;
+  } else {
+    s += __expf(x - m);
+  }
+}
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os) {
+  const float mm = fmaxf(m, om);
+  if (mm == -INFINITY) {
+    m = -INFINITY;
+    s = 0.0f;
+    return;
+  }
+  s = (m == -INFINITY ? 0.0f : s * __expf(m - mm)) + (om == -INFINITY ? 0.0f : os * __expf(om - mm));
+  m = mm;
+}
+
+__device__ __forceinline__ bool mask_allows(const uint32_t* __restrict__ mask_row, int64_t gv) {
+  return (mask_row[gv >> 5] >> (uint32_t)(gv & 31)) & 1u;
+}
+
+}  // namespace fsk

@@ -1,0 +1,98 @@
+// fs_kernels.h -- host-visible launch interface of the FlashSampling kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsk {
+
+enum Epilogue { EPI_FLAT = 0, EPI_GROUP = 1, EPI_STORE = 2 };
+
+struct GroupSummary {  // same layout as fs_group_summary_t
+  float lse;
+  float pmax;
+  int32_t arg;
+};
+
+// Geometry and pointers of one streaming launch (one workgroup per vocab tile).
+struct StreamParams {
+  const uint16_t* H;
+  int64_t ldh;
+  const uint16_t* W;
+  int64_t ldw;
+  int B;
+  int d;
+  int64_t V;             // rows of W in this launch
+  int64_t vocab_offset;  // global vocab id of W row 0 (noise and mask use global ids)
+  int row_offset;        // global batch row of H row 0 (noise counter and mask row)
+  float inv_t;
+  uint32_t seed_lo, seed_hi, step_lo, step_hi;
+  const uint32_t* mask;  // [B, ldm] words or null
+  int64_t ldm;
+  int n_tiles;        // = gridDim.x
+  int64_t n_mblocks;  // ceil(V / 16)
+  int nsub;           // ceil(d / 256): k sub-blocks of 256
+  int cs;             // sub-blocks per LDS chunk of H
+  int nchunk;         // ceil(nsub / cs)
+  int nbuf;           // LDS buffers for H chunks (1 or 2)
+  int h_rowstride;    // bytes per H row in LDS
+  // per-tile results, [B][n_tiles]
+  float* ws_val;
+  int32_t* ws_idx;
+  float* ws_m;
+  float* ws_s;
+  unsigned int* ticket;  // zero between launches; the last workgroup resets it
+  int32_t* out_idx;
+  GroupSummary* out_sum;
+  float* dbg_max;  // [B][n_tiles] or null
+  int32_t* dbg_arg;
+  float* logits;  // EPI_STORE: [B][ldl] fp32
+  int64_t ldl;
+};
+
+struct SampleParams {  // unfused second pass: sample from stored logits
+  const float* logits;
+  int64_t ldl;
+  int B;
+  int64_t V;
+  float inv_t;
+  uint32_t seed_lo, seed_hi, step_lo, step_hi;
+  const uint32_t* mask;
+  int64_t ldm;
+  int n_tiles;
+  float* ws_val;
+  int32_t* ws_idx;
+  unsigned int* ticket;
+  int32_t* out_idx;
+};
+
+// Kernel selection for a streaming launch.
+struct StreamConfig {
+  bool dot;     // dot-product kernel (else MFMA)
+  int nb;       // MFMA: 16-wide batch blocks (1, 2, 4)
+  int bd;       // dot: padded batch (1, 2, 4, 8)
+  int mb;       // 16-row vocab blocks per wave per round
+  int lds_bytes;
+};
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kLdsMax = 160 * 1024 - 256;  // leaves room for the kernels' static LDS
+constexpr int kMaxStagePieces = 8;  // 16-byte H pieces per thread held for the next LDS chunk
+constexpr int kDotMaxB = 8;
+constexpr int kMfmaMaxB = 64;
+
+// Fills the K/LDS geometry fields of p and the LDS size of cfg; returns false
+// if the shape does not fit the kernels' LDS budget.
+bool plan_stream(StreamParams& p, StreamConfig& cfg);
+
+hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream);
+hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream);
+hipError_t launch_group_combine(const GroupSummary* s, int n_groups, int B, uint64_t seed, uint64_t step, int mode,
+                                int32_t* out_idx, hipStream_t stream);
+hipError_t launch_debug_philox(uint64_t seed, uint64_t step, uint32_t row, int64_t v0, int64_t n, uint32_t* r_out,
+                               float* g_out, hipStream_t stream);
+hipError_t launch_debug_gumbel_bits(uint64_t r0, int64_t n, float* g_out, hipStream_t stream);
+hipError_t launch_debug_gumbel_scan(unsigned long long* stats, hipStream_t stream);
+
+}  // namespace fsk

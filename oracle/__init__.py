@@ -45,6 +45,7 @@ def lib():
             "fso_argmax": (i64, [P, i64]),
             "fso_sample_from_logits": (None, [P, i32, i64, f32, u64, u64, P, i64, i32, P, P]),
             "fso_sample_steps": (None, [P, i32, i64, f32, u64, u64, i64, P, i64, i32, P]),
+            "fso_sample_rows_steps": (None, [P, P, i32, i64, f32, u64, u64, i64, P, i64, i32, P, P]),
             "fso_tile_maxima": (None, [P, i32, i64, f32, u64, u64, P, i64, P, i32, P, P]),
             "fso_group_summary": (None, [P, i32, i64, i64, i64, f32, u64, u64, P, i64, P, P, P]),
             "fso_group_combine": (None, [P, P, P, i32, i32, u64, u64, i32, P]),
@@ -181,6 +182,24 @@ def sample_steps(L, T, seed, step0, nsteps, mask=None, top_k=0):
     out = np.empty((nsteps, B), np.int32)
     lib().fso_sample_steps(_ptr(L), B, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, _ptr(out))
     return out
+
+
+def sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None, top_k=0):
+    """Samples of global rows `rows` (logits L[i] belong to row rows[i]) for nsteps steps.
+
+    Returns (ids, pmax), each [nsteps, R].  mask, if given, is the full [B, ldm] mask.
+    """
+    L = _c(L, np.float32)
+    R, V = L.shape
+    rows = _c(rows, np.int32)
+    assert rows.shape == (R,)
+    m = None if mask is None else _c(mask, np.uint32)
+    ldm = 0 if m is None else m.shape[1]
+    ids = np.empty((nsteps, R), np.int32)
+    pmax = np.empty((nsteps, R), np.float32)
+    lib().fso_sample_rows_steps(_ptr(L), _ptr(rows), R, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, _ptr(ids),
+                                _ptr(pmax))
+    return ids, pmax
 
 
 def tile_maxima(L, T, seed, step, bounds, mask=None):

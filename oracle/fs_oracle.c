@@ -311,6 +311,27 @@ void fso_sample_steps(const float* logits, int B, int64_t V, float T, uint64_t s
   }
 }
 
+/* Samples of selected rows over steps step0 .. step0+nsteps-1.  logits is
+ * [R, V] holding the logits of global batch rows rows[0..R-1]; the noise and
+ * the mask row use the global row id.  out_idx and out_pmax are [nsteps, R]:
+ * the sampled id and its perturbed score. */
+void fso_sample_rows_steps(const float* logits, const int32_t* rows, int R, int64_t V, float T, uint64_t seed,
+                           uint64_t step0, int64_t nsteps, const uint32_t* mask, int64_t ldm, int top_k,
+                           int32_t* out_idx, float* out_pmax) {
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t t = 0; t < nsteps; ++t) {
+    for (int i = 0; i < R; ++i) {
+      float* p = (float*)malloc((size_t)V * sizeof(float));
+      fso_perturbed_row(logits + (int64_t)i * V, V, T, seed, step0 + (uint64_t)t, rows[i],
+                        mask ? mask + (int64_t)rows[i] * ldm : NULL, top_k, p);
+      int64_t a = fso_argmax(p, V);
+      out_idx[t * R + i] = (int32_t)a;
+      out_pmax[t * R + i] = a < 0 ? -INFINITY : p[a];
+      free(p);
+    }
+  }
+}
+
 /* Per-tile maxima of perturbed scores for one step: tiles are the vocab
  * ranges [bounds[i], bounds[i+1]).  Outputs are [B, n_tiles]. */
 void fso_tile_maxima(const float* logits, int B, int64_t V, float T, uint64_t seed, uint64_t step,
