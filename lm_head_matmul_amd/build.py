@@ -6,7 +6,9 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "fs_api.hip"), os.path.join(CSRC, "fs_kernels.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fs_api.hip", "fs_kernels.hip", "fs_stream_flat.hip",
+                                           "fs_stream_group.hip", "fs_stream_store.hip")]
+OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libflashsampling.so")
 
 HIPCC_FLAGS = [
@@ -14,7 +16,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     # packed fp32 vector ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -29,19 +30,34 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libflashsampling.so)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _check(proc, what):
+    out, err = proc.communicate()
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+    err = "\n".join(l for l in err.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{err}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared library."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.basename(src).replace(".hip", ".o"))
+        objs.append(obj)
+        procs.append((_run([hipcc(), *HIPCC_FLAGS, *inc, "-c", src, "-o", obj], verbose), src))
+    for proc, src in procs:
+        _check(proc, src)
+    tmp = LIB + ".tmp"
+    _check(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose), "link")
     os.replace(tmp, LIB)
     return LIB
 

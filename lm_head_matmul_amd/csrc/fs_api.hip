@@ -81,7 +81,7 @@ int pow2_at_least(int x) {
 
 // Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB).
 int choose_config(int B, int path, fsk::StreamConfig& cfg) {
-  const int dot_max = env_int("FS_DOT_MAX_B", 4);
+  const int dot_max = env_int("FS_DOT_MAX_B", fsk::kDotMaxB);
   bool dot;
   if (path == FS_PATH_DOT) {
     if (B > fsk::kDotMaxB) return fail(FS_ERR_UNSUPPORTED, "dot-product path supports B <= %d (got %d)", fsk::kDotMaxB, B);
@@ -94,7 +94,7 @@ int choose_config(int B, int path, fsk::StreamConfig& cfg) {
   cfg.dot = dot;
   cfg.bd = dot ? pow2_at_least(B) : 0;
   cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : 4);
-  cfg.mb = (!dot && env_int("FS_MFMA_MB", 1) == 2) ? 2 : 1;
+  cfg.fast = false;
   cfg.lds_bytes = 0;
   return FS_OK;
 }

@@ -36,6 +36,8 @@ struct StreamParams {
   int nchunk;         // ceil(nsub / cs)
   int nbuf;           // LDS buffers for H chunks (1 or 2)
   int h_rowstride;    // bytes per H row in LDS
+  int mask_words;     // mask words per row staged in LDS (0: read the mask from global memory)
+  int mask_lds_off;   // byte offset of the staged mask in LDS
   // per-tile results, [B][n_tiles]
   float* ws_val;
   int32_t* ws_idx;
@@ -70,8 +72,8 @@ struct SampleParams {  // unfused second pass: sample from stored logits
 struct StreamConfig {
   bool dot;     // dot-product kernel (else MFMA)
   int nb;       // MFMA: 16-wide batch blocks (1, 2, 4)
-  int bd;       // dot: padded batch (1, 2, 4, 8)
-  int mb;       // 16-row vocab blocks per wave per round
+  int bd;       // dot: padded batch (1, 2)
+  bool fast;    // straight-line fast driver (see fs_stream.h)
   int lds_bytes;
 };
 
@@ -79,7 +81,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kLdsMax = 160 * 1024 - 256;  // leaves room for the kernels' static LDS
 constexpr int kMaxStagePieces = 8;  // 16-byte H pieces per thread held for the next LDS chunk
-constexpr int kDotMaxB = 8;
+constexpr int kDotMaxB = 2;
+constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
+constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
 
 // Fills the K/LDS geometry fields of p and the LDS size of cfg; returns false
@@ -87,6 +91,8 @@ constexpr int kMfmaMaxB = 64;
 bool plan_stream(StreamParams& p, StreamConfig& cfg);
 
 hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream);
+template <int EPI>
+hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& cfg, hipStream_t stream);
 hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream);
 hipError_t launch_group_combine(const GroupSummary* s, int n_groups, int B, uint64_t seed, uint64_t step, int mode,
                                 int32_t* out_idx, hipStream_t stream);

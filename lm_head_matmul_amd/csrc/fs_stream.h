@@ -1,0 +1,792 @@
+// fs_stream.h -- the streaming FMMS kernels for MI355X (gfx950 / CDNA4).
+//
+// Fused LM-head matmul + sample (FMMS): logits are computed tile by tile on
+// chip, Gumbel noise is added, each vocabulary tile keeps one (value, index)
+// maximizer per row, and a small reduction over tiles yields the sample; the
+// [B, V] logits never reach HBM.  Exact because argmax decomposes over a
+// partition of the vocabulary.  [FlashSampling, arXiv 2603.15854, abstract;
+// readus.org FlashSampling summary, section on the two-stage FMMS kernel]
+//
+// Layout on the device (one persistent workgroup of 8 waves per vocab tile):
+//  * A tile is a contiguous, balanced range of 16-row vocab blocks.  Each round
+//    a wave owns MB blocks (16 * MB rows) and streams their rows of W straight
+//    from HBM into VGPRs in the MFMA operand layout: lane (r, g) = (lane % 16,
+//    lane / 16) reads 128 contiguous bytes of row r per 256-wide k sub-block,
+//    as eight 16-byte loads (k chunks 8g .. 8g + 7).  Eight MFMA k-steps then
+//    consume chunk 8g + j from lane group g at step j; the same k permutation
+//    is used for H, so each MFMA still sums over 32 matching k values.
+//  * H (the small operand) sits in LDS: the whole [B, d] when it fits,
+//    otherwise k-chunks double-buffered across the round, prefetched into
+//    registers one chunk ahead.  Rows are padded by 16 bytes so the B-operand
+//    reads of 16 lanes land in distinct banks.
+//  * Epilogue per round, on the accumulators: scale by 1/T, mask, Philox4x32-10
+//    noise (one call covers the four consecutive vocab ids a lane holds), argmax
+//    update.  Per tile, the winners go to a [B, n_tiles] workspace; the last
+//    workgroup to finish (device-scope ticket) reduces over tiles.
+#pragma once
+
+#include <atomic>
+
+#include "fs_device.h"
+#include "fs_kernels.h"
+
+namespace fsk {
+
+// ---------------------------------------------------------------------------
+// Cross-tile reduction by the last workgroup to finish.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__device__ void finish_tiles(const int B, const int n_tiles, const float* __restrict__ ws_val,
+                             const int32_t* __restrict__ ws_idx, const float* __restrict__ ws_m,
+                             const float* __restrict__ ws_s, unsigned int* ticket, int32_t* out_idx,
+                             GroupSummary* out_sum) {
+  // Publication protocol: the barrier orders every thread's workspace stores
+  // before thread 0's device-scope release increment; only the workgroup that
+  // takes the last ticket performs the matching device-scope acquire.  (An
+  // acquire in every workgroup would invalidate each XCD's L2 under the
+  // workgroups still streaming W.)
+  __shared__ int s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (unsigned)(n_tiles - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int b = wave; b < B; b += kWaves) {
+    float v = -INFINITY, m = -INFINITY, s = 0.0f;
+    int32_t i = -1;
+    for (int t = lane; t < n_tiles; t += 64) {
+      const int64_t o = (int64_t)b * n_tiles + t;
+      merge_best(v, i, ws_val[o], ws_idx[o]);
+      if (EPI == EPI_GROUP) lse_merge(m, s, ws_m[o], ws_s[o]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(v, off);
+      const int32_t oi = __shfl_xor(i, off);
+      merge_best(v, i, ov, oi);
+      if (EPI == EPI_GROUP) {
+        const float om = __shfl_xor(m, off);
+        const float os = __shfl_xor(s, off);
+        lse_merge(m, s, om, os);
+      }
+    }
+    if (lane == 0) {
+      if (EPI == EPI_GROUP) {
+        GroupSummary g;
+        g.lse = (m == -INFINITY) ? -INFINITY : m + logf(s);
+        g.pmax = v;
+        g.arg = i;
+        out_sum[b] = g;
+      } else {
+        out_idx[b] = i;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Per-wave results (already reduced inside the wave) sit in LDS scratch as
+// [kWaves][Bp] (val, idx, m, s); reduce over waves and publish the tile's entry.
+template <int EPI>
+__device__ void publish_tile(const StreamParams& p, const int Bp, const float* sv, const int32_t* si, const float* sm,
+                             const float* ss) {
+  const int tile = blockIdx.x;
+  for (int b = threadIdx.x; b < p.B; b += kThreads) {
+    float v = -INFINITY, m = -INFINITY, s = 0.0f;
+    int32_t i = -1;
+    for (int w = 0; w < kWaves; ++w) {
+      merge_best(v, i, sv[w * Bp + b], si[w * Bp + b]);
+      if (EPI == EPI_GROUP) lse_merge(m, s, sm[w * Bp + b], ss[w * Bp + b]);
+    }
+    const int64_t o = (int64_t)b * p.n_tiles + tile;
+    p.ws_val[o] = v;
+    p.ws_idx[o] = i;
+    if (EPI == EPI_GROUP) {
+      p.ws_m[o] = m;
+      p.ws_s[o] = s;
+    }
+    if (p.dbg_max) {
+      p.dbg_max[o] = v;
+      p.dbg_arg[o] = i;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the streaming kernels.
+// ---------------------------------------------------------------------------
+struct TileRange {
+  int64_t mb_lo, mb_hi;
+  int rounds;
+};
+
+__device__ __forceinline__ TileRange tile_range(const StreamParams& p) {
+  TileRange t;
+  t.mb_lo = (int64_t)blockIdx.x * p.n_mblocks / p.n_tiles;
+  t.mb_hi = (int64_t)(blockIdx.x + 1) * p.n_mblocks / p.n_tiles;
+  t.rounds = (int)((t.mb_hi - t.mb_lo + kWaves - 1) / kWaves);
+  return t;
+}
+
+// H chunk `cidx` (k in [cidx*cs*256, ...)) as 16-byte pieces: piece P = n * (cs*32) + q.
+// The load is unconditional (row and k clamped into H); h_valid says whether
+// the piece lies inside H (pieces outside are stored as zero).
+__device__ __forceinline__ u32x4_t h_load(const StreamParams& p, int cidx, int P) {
+  const int per_row = p.cs * 32;
+  const int n = P / per_row;
+  const int q = P - n * per_row;
+  const int k = cidx * p.cs * 256 + q * 8;
+  const int nc = n < p.B ? n : p.B - 1;
+  const int kc = k < p.d ? k : p.d - 8;
+  return *(const u32x4_t*)(p.H + (int64_t)nc * p.ldh + kc);
+}
+
+__device__ __forceinline__ bool h_valid(const StreamParams& p, int cidx, int P) {
+  const int per_row = p.cs * 32;
+  const int n = P / per_row;
+  const int k = cidx * p.cs * 256 + (P - n * per_row) * 8;
+  return n < p.B && k < p.d;
+}
+
+__device__ __forceinline__ void h_store(const StreamParams& p, unsigned char* buf, int P, u32x4_t v) {
+  const int per_row = p.cs * 32;
+  const int n = P / per_row;
+  const int q = P - n * per_row;
+  *(u32x4_t*)(buf + n * p.h_rowstride + q * 16) = v;
+}
+
+// Stages the whole chunk (all pieces) directly.
+__device__ void h_stage_all(const StreamParams& p, int Bp, int cidx, unsigned char* buf) {
+  const int np = Bp * p.cs * 32;
+  for (int P = threadIdx.x; P < np; P += kThreads) {
+    const u32x4_t v = h_load(p, cidx, P);
+    h_store(p, buf, P, h_valid(p, cidx, P) ? v : u32x4_t{0u, 0u, 0u, 0u});
+  }
+}
+
+// Prefetch of the next chunk into registers: raw, unconditional loads (so the
+// W stream in flight is never drained by a wait); masking happens at commit.
+__device__ __forceinline__ void h_prefetch(u32x4_t (&hs)[kMaxStagePieces], const StreamParams& p, int Bp, int cidx) {
+  const int np = Bp * p.cs * 32;
+#pragma unroll
+  for (int i = 0; i < kMaxStagePieces; ++i) {
+    const int P = threadIdx.x + i * kThreads;
+    hs[i] = h_load(p, cidx, P < np ? P : np - 1);
+  }
+}
+
+__device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], const StreamParams& p, int Bp, int cidx,
+                                         unsigned char* buf) {
+  const int np = Bp * p.cs * 32;
+#pragma unroll
+  for (int i = 0; i < kMaxStagePieces; ++i) {
+    const int P = threadIdx.x + i * kThreads;
+    if (P < np) h_store(p, buf, P, h_valid(p, cidx, P) ? hs[i] : u32x4_t{0u, 0u, 0u, 0u});
+  }
+}
+
+// The vocabulary mask of the tile, staged in LDS at kernel start (when it fits,
+// p.mask_words > 0): rows b < B, words [w_lo, w_lo + p.mask_words) of each row.
+// Reading mask bits from LDS keeps global loads out of the epilogue: the
+// vector-memory counter is in order, so waiting for one mask word would also
+// wait for every W prefetch issued before it.
+__device__ __forceinline__ int64_t mask_w_lo(const StreamParams& p, const TileRange& tr) {
+  return (p.vocab_offset + tr.mb_lo * 16) >> 5;
+}
+
+__device__ void mask_stage(const StreamParams& p, const TileRange& tr, uint32_t* lds) {
+  if (!p.mask || p.mask_words == 0) return;
+  const int64_t w_lo = mask_w_lo(p, tr);
+  const int64_t w_max = (p.vocab_offset + p.V - 1) >> 5;  // last word of the launch's vocabulary
+  const int n = p.B * p.mask_words;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int b = i / p.mask_words;
+    const int64_t w = w_lo + (i - b * p.mask_words);
+    lds[i] = w <= w_max ? p.mask[((int64_t)p.row_offset + b) * p.ldm + w] : 0u;
+  }
+}
+
+// Four mask bits of vocab ids gv0 .. gv0+3 (gv0 % 4 == 0) of local row b.
+__device__ __forceinline__ uint32_t mask_bits4(const StreamParams& p, const uint32_t* lds, int64_t w_lo, int64_t gv0,
+                                               int b) {
+  if (!p.mask) return 0xFu;
+  uint32_t word;
+  if (p.mask_words > 0)
+    word = lds[b * p.mask_words + (int)((gv0 >> 5) - w_lo)];
+  else
+    word = p.mask[((int64_t)p.row_offset + b) * p.ldm + (gv0 >> 5)];
+  return (word >> (uint32_t)(gv0 & 31)) & 0xFu;
+}
+
+// Perturbed scores of the four consecutive vocab ids v0 .. v0+3 (local ids,
+// v0 % 4 == 0) of row b, given their raw logits and mask bits; updates the
+// running maximizer (and the log-sum-exp state in grouped mode).  The scan
+// order of a lane is increasing in v, so a strict comparison keeps the lowest
+// id on ties.
+template <int EPI>
+__device__ __forceinline__ void epilogue_quad(const StreamParams& p, int64_t v0, int b, const float (&acc)[4],
+                                              uint32_t bits, float& bv, int32_t& bi, float& lm, float& ls) {
+  const int64_t gv0 = p.vocab_offset + v0;
+  const int64_t grow = (int64_t)p.row_offset + b;
+  const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)(gv0 >> 2), (uint32_t)grow, p.step_lo, p.step_hi);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = (v0 + i < p.V) && ((bits >> i) & 1u);
+    const float s = acc[i] * p.inv_t;
+    const float pv = ok ? s + gumbel_from_bits(r.w[i]) : -INFINITY;
+    if (pv > bv) {
+      bv = pv;
+      bi = (int32_t)(gv0 + i);
+    }
+    if (EPI == EPI_GROUP && ok) lse_push(lm, ls, s);
+  }
+}
+
+// Lane's W row pointer for vocab block `mb` (rows past the tile or past V are
+// clamped to the tile's last row; their results are never used).
+__device__ __forceinline__ const uint16_t* w_row(const StreamParams& p, const TileRange& tr, int64_t mb, int l16) {
+  const int64_t tile_end = (tr.mb_hi * 16 < p.V ? tr.mb_hi * 16 : p.V);
+  int64_t row = mb * 16 + l16;
+  row = row < tile_end ? row : tile_end - 1;
+  return p.W + row * p.ldw;
+}
+
+// ---------------------------------------------------------------------------
+// Streaming drivers.  Both call
+//   body(cur, hbase, sbc, r, t)  -- consume sub-block t (0 .. nsub-1) of round r;
+//                                   hbase/sbc locate its H slice in LDS
+//   round_end(r)                 -- after the last sub-block of round r
+// Wave w of the workgroup owns vocab block mb_lo + r * 8 + w in round r.
+//
+// Fast driver (d % (256 U) == 0; chunked H only with chunks of exactly U
+// sub-blocks): rounds are split into groups of U sub-blocks whose bodies run
+// unconditionally, with a ring of U register buffers: while sub-block t is
+// consumed the loads of t + 1 .. t + U - 1 are in flight (they run on into the
+// next round).  The loop body has no data-dependent branches, so the
+// compiler's wait counters stay exact and no prefetch is ever drained.
+// ---------------------------------------------------------------------------
+template <int U, bool RESIDENT, class Body, class RoundEnd>
+__device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const TileRange& tr, int Bp,
+                                                   unsigned char* smem, Body&& body, RoundEnd&& round_end) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int nsub = p.nsub, ngrp = nsub / U;
+  const int bufbytes = Bp * p.h_rowstride;
+  if (tr.rounds == 0) return;
+
+  auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
+    const u32x4_t* src = (const u32x4_t*)(w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16) + sb * 256 +
+                                          grp * 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) buf[e] = src[e];
+  };
+  int lr = 0, lsb = 0;  // next position to load; stays on the last sub-block past the end
+  auto advance = [&]() {
+    if (++lsb == nsub) {
+      lsb = 0;
+      ++lr;
+    }
+    if (lr >= tr.rounds) {
+      lr = tr.rounds - 1;
+      lsb = nsub - 1;
+    }
+  };
+
+  u32x4_t hs[kMaxStagePieces];
+  if (RESIDENT) {
+    h_stage_all(p, Bp, 0, smem);
+  } else {
+    h_prefetch(hs, p, Bp, 0);
+    h_commit(hs, p, Bp, 0, smem);
+  }
+  __syncthreads();
+
+  u32x4_t buf[U][8];
+#pragma unroll
+  for (int k = 0; k < U - 1; ++k) {
+    load(buf[k], lr, lsb);
+    advance();
+  }
+  int cc = 0;  // chunks consumed (chunked H: one chunk per group)
+  for (int r = 0; r < tr.rounds; ++r) {
+    for (int g = 0; g < ngrp; ++g) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        load(buf[(k + U - 1) % U], lr, lsb);
+        advance();
+        // the chunk after this one (chunk index == group index); past the last
+        // group of the last round this stages an unused copy of chunk 0
+        if (!RESIDENT && k == 0) h_prefetch(hs, p, Bp, g + 1 < ngrp ? g + 1 : 0);
+        // keep the loads above ahead of the compute below: the scheduler would
+        // otherwise sink them under the MFMAs to save registers
+        __builtin_amdgcn_sched_barrier(0);
+        if (RESIDENT)
+          body(buf[k], smem, g * U + k, r, g * U + k);
+        else
+          body(buf[k], smem + (cc & 1) * bufbytes, k, r, g * U + k);
+        if (!RESIDENT && k == U - 1) {
+          h_commit(hs, p, Bp, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
+          __syncthreads();
+          ++cc;
+        }
+      }
+    }
+    round_end(r);
+  }
+}
+
+// General driver: any d (k tail clamped into the row's last chunk, which meets
+// zeros in the staged H), any chunking, two register buffers.  Conditions are
+// evaluated per sub-block.
+template <bool RESIDENT, class Body, class RoundEnd>
+__device__ __forceinline__ void stream_driver_general(const StreamParams& p, const TileRange& tr, int Bp,
+                                                      unsigned char* smem, Body&& body, RoundEnd&& round_end) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int nsub = p.nsub, d = p.d;
+  const int cs = RESIDENT ? nsub : p.cs;
+  const int nchunk = RESIDENT ? 1 : p.nchunk;
+  const int bufbytes = Bp * p.h_rowstride;
+  if (tr.rounds == 0) return;
+
+  auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
+    const uint16_t* base = w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = sb * 256 + grp * 64 + e * 8;
+      buf[e] = *(const u32x4_t*)(base + (k < d ? k : d - 8));
+    }
+  };
+
+  u32x4_t hs[kMaxStagePieces];
+  if (RESIDENT) {
+    h_stage_all(p, Bp, 0, smem);
+  } else {
+    h_prefetch(hs, p, Bp, 0);
+    h_commit(hs, p, Bp, 0, smem);
+  }
+  __syncthreads();
+
+  u32x4_t w0[8], w1[8];
+  int r = 0, sb = 0, cidx = 0, sbc = 0, cc = 0;
+  int lr = 0, lsb = 0;
+  auto advance = [&]() {
+    if (++lsb == nsub) {
+      lsb = 0;
+      ++lr;
+    }
+    if (lr >= tr.rounds) {
+      lr = tr.rounds - 1;
+      lsb = nsub - 1;
+    }
+  };
+  load(w0, lr, lsb);
+  advance();
+
+  auto step = [&](const u32x4_t (&cur)[8], u32x4_t (&nxt)[8]) {
+    load(nxt, lr, lsb);
+    advance();
+    __builtin_amdgcn_sched_barrier(0);
+    if (RESIDENT) {
+      body(cur, smem, sb, r, sb);
+    } else {
+      const bool chunk_end = (sbc == cs - 1 || sb == nsub - 1);
+      const bool last_chunk = (r == tr.rounds - 1) && (cidx == nchunk - 1);
+      const int next_c = cidx + 1 < nchunk ? cidx + 1 : 0;
+      if (sbc == 0 && !last_chunk) h_prefetch(hs, p, Bp, next_c);
+      body(cur, smem + ((p.nbuf == 2) ? (cc & 1) : 0) * bufbytes, sbc, r, sb);
+      if (chunk_end) {
+        if (!last_chunk) {
+          if (p.nbuf == 2) {
+            h_commit(hs, p, Bp, next_c, smem + ((cc + 1) & 1) * bufbytes);
+            __syncthreads();
+          } else {
+            __syncthreads();
+            h_commit(hs, p, Bp, next_c, smem);
+            __syncthreads();
+          }
+        }
+        ++cc;
+        ++cidx;
+        sbc = 0;
+      } else {
+        ++sbc;
+      }
+      if (sb == nsub - 1) {
+        cidx = 0;
+        sbc = 0;
+      }
+    }
+    if (sb == nsub - 1) round_end(r);
+    if (++sb == nsub) {
+      sb = 0;
+      ++r;
+    }
+  };
+
+  const int total = tr.rounds * nsub;
+  for (int it = 0; it < total; it += 2) {
+    step(w0, w1);
+    if (it + 1 < total) step(w1, w0);
+  }
+}
+
+template <bool FAST, bool RESIDENT, int RING, class Body, class RoundEnd>
+__device__ __forceinline__ void stream_driver(const StreamParams& p, const TileRange& tr, int Bp, unsigned char* smem,
+                                              Body&& body, RoundEnd&& round_end) {
+  if (FAST)
+    stream_driver_fast<RING, RESIDENT>(p, tr, Bp, smem, body, round_end);
+  else
+    stream_driver_general<RESIDENT>(p, tr, Bp, smem, body, round_end);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA streaming kernel (batch padded to 16 * NB columns).
+//
+// Deferred epilogue: at the end of round r the accumulators move to a pending
+// set, and N-block n of that set is finished (scale, mask, noise, argmax) in
+// body n of round r + 1, right after that body's MFMAs; the last round is
+// finished after the stream.  The ALU work of the epilogue is thereby spread
+// over bodies whose W loads are already in flight.
+// ---------------------------------------------------------------------------
+template <int NB, int EPI, bool RESIDENT, bool FAST, int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
+__global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int Bp = NB * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const TileRange tr = tile_range(p);
+  const int rs = p.h_rowstride;
+  uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
+  const int64_t mw_lo = mask_w_lo(p, tr);
+  mask_stage(p, tr, mask_lds);  // made visible by the driver's first barrier
+
+  float bv[NB], lm[NB], ls[NB];
+  int32_t bi[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    bv[nb] = -INFINITY;
+    bi[nb] = -1;
+    lm[nb] = -INFINITY;
+    ls[nb] = 0.0f;
+  }
+  f32x4_t acc[NB], pend[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    pend[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One sub-block: 8 k-steps; with NB <= 2 the B operands of step j + 1 are
+  // read from LDS while the MFMAs of step j run (with NB = 4 the registers are
+  // needed elsewhere and the reads are left to the scheduler).
+  auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc) {
+    const unsigned char* hb = hbase + sbc * 512 + grp * 128 + l16 * rs;
+    if (NB > 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const u32x4_t hv = *(const u32x4_t*)(hb + nb * 16 * rs + j * 16);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
+                                                            __builtin_bit_cast(bf16x8_t, hv), acc[nb], 0, 0, 0);
+        }
+      return;
+    }
+    u32x4_t h0[NB], h1[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + nb * 16 * rs);
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + nb * 16 * rs + (j + 1) * 16);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
+                                                          __builtin_bit_cast(bf16x8_t, h0[nb]), acc[nb], 0, 0, 0);
+      if (j + 2 < 8) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + nb * 16 * rs + (j + 2) * 16);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j + 1]),
+                                                          __builtin_bit_cast(bf16x8_t, h1[nb]), acc[nb], 0, 0, 0);
+    }
+  };
+
+  // Finish N-block nb of the pending accumulators of round rnd.
+  auto finish_nb = [&](int rnd, int nb) {
+    const int64_t mbg = tr.mb_lo + (int64_t)rnd * kWaves + wave;
+    if (mbg >= tr.mb_hi) return;
+    const int64_t v0 = mbg * 16 + grp * 4;
+    const int b = nb * 16 + l16;
+    if (b >= p.B) return;
+    const float a4[4] = {pend[nb][0], pend[nb][1], pend[nb][2], pend[nb][3]};
+    if (EPI == EPI_STORE) {
+      float* dst = p.logits + (int64_t)b * p.ldl + v0;
+      if (v0 + 3 < p.V) {
+        *(f32x4_t*)dst = pend[nb];
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (v0 + i < p.V) dst[i] = a4[i];
+      }
+    } else {
+      const uint32_t bits = mask_bits4(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
+      epilogue_quad<EPI>(p, v0, b, a4, bits, bv[nb], bi[nb], lm[nb], ls[nb]);
+    }
+  };
+
+  auto body = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc, int r, int t) {
+    compute(cur, hbase, sbc);
+    if (r > 0 && t < NB) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (nb == t) finish_nb(r - 1, nb);
+    }
+  };
+  // With fewer sub-blocks per round than N-blocks, the pending set is finished at once.
+  auto round_end = [&](int r) {
+    if (r > 0 && p.nsub < NB) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (nb >= p.nsub) finish_nb(r - 1, nb);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      pend[nb] = acc[nb];
+      acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  stream_driver<FAST, RESIDENT, RING>(p, tr, Bp, smem, body, round_end);
+  if (tr.rounds > 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) finish_nb(tr.rounds - 1, nb);
+  }
+  if (EPI == EPI_STORE) return;
+
+  // Reduce inside the wave: lanes l16, l16 + 16, l16 + 32, l16 + 48 share a column.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float ov = __shfl_xor(bv[nb], off);
+      const int32_t oi = __shfl_xor(bi[nb], off);
+      merge_best(bv[nb], bi[nb], ov, oi);
+      if (EPI == EPI_GROUP) {
+        const float om = __shfl_xor(lm[nb], off);
+        const float os = __shfl_xor(ls[nb], off);
+        lse_merge(lm[nb], ls[nb], om, os);
+      }
+    }
+  }
+  __syncthreads();  // H buffers are free: reuse LDS as scratch
+  float* sv = (float*)smem;
+  int32_t* si = (int32_t*)(sv + kWaves * Bp);
+  float* sm = (float*)(si + kWaves * Bp);
+  float* ss = sm + kWaves * Bp;
+  if (grp == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = nb * 16 + l16;
+      sv[wave * Bp + b] = bv[nb];
+      si[wave * Bp + b] = bi[nb];
+      sm[wave * Bp + b] = lm[nb];
+      ss[wave * Bp + b] = ls[nb];
+    }
+  }
+  __syncthreads();
+  publish_tile<EPI>(p, Bp, sv, si, sm, ss);
+  finish_tiles<EPI>(p.B, p.n_tiles, p.ws_val, p.ws_idx, p.ws_m, p.ws_s, p.ticket, p.out_idx, p.out_sum);
+}
+
+// ---------------------------------------------------------------------------
+// Dot-product streaming kernel for small batches (B <= BD <= 2): the same W
+// stream, with bf16 pair dot products on the vector ALU against H rows read
+// from LDS (one address per 16-lane group, i.e. broadcast reads).  The four
+// lane groups are summed (two cross-lane steps) in the deferred epilogue;
+// lane (r, g) then handles row r for batch row g.
+// ---------------------------------------------------------------------------
+// The bf16 pairs are taken with shufflevector from the 8-wide bf16 view: a
+// bit_cast of each 32-bit vector element to bf16x2 is miscompiled by this
+// toolchain (every call then reads element 0).
+__device__ __forceinline__ float dot8(const u32x4_t w, const u32x4_t h, float c) {
+  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w);
+  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, h);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), c, false);
+  return c;
+}
+
+template <int BD, int EPI, bool RESIDENT, bool FAST, int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
+__global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p) {
+  static_assert(BD <= 2, "dot kernel handles at most 2 batch rows");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const TileRange tr = tile_range(p);
+  const int rs = p.h_rowstride;
+  uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
+  const int64_t mw_lo = mask_w_lo(p, tr);
+  mask_stage(p, tr, mask_lds);
+
+  float bv = -INFINITY, lm = -INFINITY, ls = 0.0f;
+  int32_t bi = -1;
+  float acc[BD], pend[BD];
+#pragma unroll
+  for (int b = 0; b < BD; ++b) {
+    acc[b] = 0.0f;
+    pend[b] = 0.0f;
+  }
+
+  auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc) {
+    const unsigned char* hb = hbase + sbc * 512 + grp * 128;
+    u32x4_t h0[BD], h1[BD];
+#pragma unroll
+    for (int b = 0; b < BD; ++b) h0[b] = *(const u32x4_t*)(hb + b * rs);
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+#pragma unroll
+      for (int b = 0; b < BD; ++b) h1[b] = *(const u32x4_t*)(hb + b * rs + (j + 1) * 16);
+#pragma unroll
+      for (int b = 0; b < BD; ++b) acc[b] = dot8(cur[j], h0[b], acc[b]);
+      if (j + 2 < 8) {
+#pragma unroll
+        for (int b = 0; b < BD; ++b) h0[b] = *(const u32x4_t*)(hb + b * rs + (j + 2) * 16);
+      }
+#pragma unroll
+      for (int b = 0; b < BD; ++b) acc[b] = dot8(cur[j + 1], h1[b], acc[b]);
+    }
+  };
+
+  auto finish_round = [&](int rnd) {
+    float x[BD];
+#pragma unroll
+    for (int b = 0; b < BD; ++b) {
+      x[b] = pend[b] + __shfl_xor(pend[b], 16);
+      x[b] += __shfl_xor(x[b], 32);
+    }
+    const int64_t mbg = tr.mb_lo + (int64_t)rnd * kWaves + wave;
+    const int b = grp;
+    if (mbg >= tr.mb_hi || b >= p.B || b >= BD) return;
+    const int64_t v = mbg * 16 + l16;
+    const int64_t gv = p.vocab_offset + v;
+    const float xv = (BD == 1 || b == 0) ? x[0] : x[BD - 1];
+    if (EPI == EPI_STORE) {
+      if (v < p.V) p.logits[(int64_t)b * p.ldl + v] = xv;
+      return;
+    }
+    const int64_t grow = (int64_t)p.row_offset + b;
+    const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)(gv >> 2), (uint32_t)grow, p.step_lo, p.step_hi);
+    const uint32_t q = (uint32_t)(gv & 3);
+    const uint32_t word = q == 0 ? r.w[0] : q == 1 ? r.w[1] : q == 2 ? r.w[2] : r.w[3];
+    const bool ok = v < p.V && ((mask_bits4(p, mask_lds, mw_lo, gv & ~(int64_t)3, b) >> q) & 1u);
+    const float sc = xv * p.inv_t;
+    const float pv = ok ? sc + gumbel_from_bits(word) : -INFINITY;
+    if (pv > bv) {
+      bv = pv;
+      bi = (int32_t)gv;
+    }
+    if (EPI == EPI_GROUP && ok) lse_push(lm, ls, sc);
+  };
+
+  auto body = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc, int r, int t) {
+    compute(cur, hbase, sbc);
+    if (r > 0 && t == 0) finish_round(r - 1);
+  };
+  auto round_end = [&](int) {
+#pragma unroll
+    for (int b = 0; b < BD; ++b) {
+      pend[b] = acc[b];
+      acc[b] = 0.0f;
+    }
+  };
+
+  stream_driver<FAST, RESIDENT, RING>(p, tr, BD, smem, body, round_end);
+  if (tr.rounds > 0) finish_round(tr.rounds - 1);
+  if (EPI == EPI_STORE) return;
+
+  // Reduce over the 16 rows of each lane group.
+#pragma unroll
+  for (int off = 1; off <= 8; off <<= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int32_t oi = __shfl_xor(bi, off);
+    merge_best(bv, bi, ov, oi);
+    if (EPI == EPI_GROUP) {
+      const float om = __shfl_xor(lm, off);
+      const float os = __shfl_xor(ls, off);
+      lse_merge(lm, ls, om, os);
+    }
+  }
+  __syncthreads();
+  float* sv = (float*)smem;
+  int32_t* si = (int32_t*)(sv + kWaves * BD);
+  float* sm = (float*)(si + kWaves * BD);
+  float* ss = sm + kWaves * BD;
+  if (l16 == 0 && grp < BD) {
+    sv[wave * BD + grp] = bv;
+    si[wave * BD + grp] = bi;
+    sm[wave * BD + grp] = lm;
+    ss[wave * BD + grp] = ls;
+  }
+  __syncthreads();
+  publish_tile<EPI>(p, BD, sv, si, sm, ss);
+  finish_tiles<EPI>(p.B, p.n_tiles, p.ws_val, p.ws_idx, p.ws_m, p.ws_s, p.ticket, p.out_idx, p.out_sum);
+}
+
+// ---------------------------------------------------------------------------
+// Launch of one streaming configuration (instantiated once per epilogue, each
+// in its own translation unit).
+// ---------------------------------------------------------------------------
+// The dynamic-LDS limit of each kernel is raised to the full budget once per
+// device (the attribute call is far slower than a launch).
+template <typename K>
+static hipError_t launch_with_lds(K kernel, int grid, int lds, hipStream_t stream, const StreamParams& p) {
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(raised.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e != hipSuccess) return e;
+    raised.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int EPI, bool RES, bool FAST>
+static hipError_t launch_variant(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
+  const int g = p.n_tiles, L = c.lds_bytes;
+  if (c.dot) {
+    switch (c.bd) {
+      case 1: return launch_with_lds(fmms_dot_kernel<1, EPI, RES, FAST>, g, L, s, p);
+      case 2: return launch_with_lds(fmms_dot_kernel<2, EPI, RES, FAST>, g, L, s, p);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (c.nb) {
+    case 1: return launch_with_lds(fmms_mfma_kernel<1, EPI, RES, FAST>, g, L, s, p);
+    case 2: return launch_with_lds(fmms_mfma_kernel<2, EPI, RES, FAST>, g, L, s, p);
+    case 4: return launch_with_lds(fmms_mfma_kernel<4, EPI, RES, FAST>, g, L, s, p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int EPI>
+hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
+  const bool res = p.nchunk == 1;
+  if (res) return c.fast ? launch_variant<EPI, true, true>(p, c, s) : launch_variant<EPI, true, false>(p, c, s);
+  return c.fast ? launch_variant<EPI, false, true>(p, c, s) : launch_variant<EPI, false, false>(p, c, s);
+}
+
+}  // namespace fsk

@@ -109,7 +109,7 @@ def test_gumbel_exhaustive_scan_finite(fs, ctx):
 # --- exact logits --------------------------------------------------------------
 
 @pytest.mark.parametrize("B,d,V,path", [
-    (5, 256, 1000, 1), (5, 256, 1000, 2), (20, 264, 777, 2), (64, 512, 1030, 2), (8, 1000, 333, 1),
+    (2, 256, 1000, 1), (5, 256, 1000, 2), (20, 264, 777, 2), (64, 512, 1030, 2), (1, 1000, 333, 1),
     (3, 2056, 515, 0), (64, 2056, 300, 2),
 ])
 def test_logits_exact_on_integer_inputs(fs, ctx, B, d, V, path):
@@ -144,10 +144,12 @@ def test_tiny_workload_parity(fs, ctx, path):
     w = synth.WORKLOADS["tiny"]
     say(f"tiny workload B={w['B']} d={w['d']} V={w['V']} path={path}, 200 steps")
     H = synth.workload_H("tiny")
+    if path == 1:  # the dot-product kernel takes at most 2 rows
+        H = H[:2]
     W = synth.workload_W("tiny")
     L = oracle.logits(H, W)
     gpu = _run_steps(fs, ctx, dev_bf16(H), dev_bf16(W), 1.0, 0, range(200), path=path)
-    rows = np.arange(w["B"])
+    rows = np.arange(H.shape[0])
     ora, _ = oracle.sample_rows_steps(L, rows, 1.0, 0, 0, 200)
     n = check_ids(gpu, ora, oracle_p_fn(L, rows, 1.0, 0, 0), "tiny")
     say(f"near-tie mismatches: {n}")
@@ -158,6 +160,8 @@ def test_tile_maxima_tiny(fs, ctx, path):
     import torch
 
     H = synth.workload_H("tiny")
+    if path == 1:
+        H = H[:2]
     W = synth.workload_W("tiny")
     L = oracle.logits(H, W)
     B, V = L.shape
@@ -176,9 +180,9 @@ def test_tile_maxima_tiny(fs, ctx, path):
 RAGGED = [
     # B, d, V, T, path
     (1, 264, 1000, 1.0, 0), (1, 264, 1000, 1.0, 2), (3, 1000, 4097, 0.7, 0), (3, 1000, 4097, 0.7, 2),
-    (7, 512, 333, 1.3, 1), (8, 512, 2000, 1.0, 0), (17, 256, 2000, 0.9, 0), (33, 520, 1234, 1.0, 0),
+    (2, 512, 333, 1.3, 1), (7, 512, 333, 1.3, 0), (8, 512, 2000, 1.0, 0), (17, 256, 2000, 0.9, 0), (33, 520, 1234, 1.0, 0),
     (48, 768, 3001, 0.7, 0), (64, 2056, 1500, 1.0, 0), (65, 256, 999, 1.0, 0), (100, 264, 777, 0.8, 0),
-    (8, 10240, 500, 1.0, 1), (2, 16, 7, 1.0, 0),
+    (2, 86016, 300, 1.0, 1), (2, 16, 7, 1.0, 0), (16, 20480, 300, 1.0, 2),
 ]
 
 
@@ -238,7 +242,7 @@ def test_masked_parity_and_no_masked_picks(fs, ctx):
         check_ids(gpu, ora, oracle_p_fn(L, rows, T, 5, 0, mask=mask), "masked")
 
 
-@pytest.mark.parametrize("B,d,V,path", [(4, 256, 4096, 1), (4, 256, 4096, 2), (40, 1024, 5000, 0),
+@pytest.mark.parametrize("B,d,V,path", [(2, 256, 4096, 1), (4, 256, 4096, 2), (40, 1024, 5000, 0),
                                         (64, 2048, 3000, 2), (130, 264, 700, 0)])
 def test_unfused_equals_fused(fs, ctx, B, d, V, path):
     import torch
@@ -276,7 +280,7 @@ def test_determinism_reruns(fs, ctx):
 
 # --- grouped ---------------------------------------------------------------------
 
-@pytest.mark.parametrize("B,d,G,n_groups,path", [(6, 256, 512, 8, 0), (64, 768, 1024, 4, 0), (3, 512, 96, 5, 1)])
+@pytest.mark.parametrize("B,d,G,n_groups,path", [(6, 256, 512, 8, 0), (64, 768, 1024, 4, 0), (2, 512, 96, 5, 1)])
 def test_grouped_summaries_and_combine(fs, ctx, B, d, G, n_groups, path):
     import torch
 
