@@ -448,11 +448,11 @@ __device__ __forceinline__ void stream_driver(const StreamParams& p, const TileR
 // ---------------------------------------------------------------------------
 // MFMA streaming kernel (batch padded to 16 * NB columns).
 //
-// Deferred epilogue: at the end of round r the accumulators move to a pending
-// set, and N-block n of that set is finished (scale, mask, noise, argmax) in
-// body n of round r + 1, right after that body's MFMAs; the last round is
-// finished after the stream.  The ALU work of the epilogue is thereby spread
-// over bodies whose W loads are already in flight.
+// Deferred epilogue (NB <= 2): at the end of round r the accumulators move to
+// a pending set, and N-block n of that set is finished (scale, mask, noise,
+// argmax) in body n of round r + 1, right after that body's MFMAs; the last
+// round is finished after the stream.  The ALU work of the epilogue is thereby
+// spread over bodies whose W loads are already in flight.
 // ---------------------------------------------------------------------------
 template <int NB, int EPI, bool RESIDENT, bool FAST, int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
@@ -482,22 +482,11 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     pend[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One sub-block: 8 k-steps; with NB <= 2 the B operands of step j + 1 are
-  // read from LDS while the MFMAs of step j run (with NB = 4 the registers are
-  // needed elsewhere and the reads are left to the scheduler).
+  // One sub-block: 8 k-steps; the B operands of step j + 1 are read from LDS
+  // while the MFMAs of step j run.  (Left to itself the compiler waits on each
+  // LDS read right before its MFMA, and the loop becomes bound by LDS latency.)
   auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc) {
     const unsigned char* hb = hbase + sbc * 512 + grp * 128 + l16 * rs;
-    if (NB > 2) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const u32x4_t hv = *(const u32x4_t*)(hb + nb * 16 * rs + j * 16);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
-                                                            __builtin_bit_cast(bf16x8_t, hv), acc[nb], 0, 0, 0);
-        }
-      return;
-    }
     u32x4_t h0[NB], h1[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + nb * 16 * rs);
@@ -505,6 +494,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     for (int j = 0; j < 8; j += 2) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + nb * 16 * rs + (j + 1) * 16);
+      __builtin_amdgcn_sched_barrier(0);  // reads of step j + 1 stay ahead of the MFMAs of step j
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
@@ -513,6 +503,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + nb * 16 * rs + (j + 2) * 16);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j + 1]),
@@ -542,17 +533,19 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
   };
 
+  // NB <= 2: deferred (see above).  NB = 4: the round is finished at its end
+  // (measured no slower, and it leaves the registers to the operand pipeline).
+  constexpr bool kDefer = NB <= 2;
   auto body = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc, int r, int t) {
     compute(cur, hbase, sbc);
-    if (r > 0 && t < NB) {
+    if (kDefer && r > 0 && t < NB) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         if (nb == t) finish_nb(r - 1, nb);
     }
   };
-  // With fewer sub-blocks per round than N-blocks, the pending set is finished at once.
   auto round_end = [&](int r) {
-    if (r > 0 && p.nsub < NB) {
+    if (kDefer && r > 0 && p.nsub < NB) {  // fewer sub-blocks per round than N-blocks
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         if (nb >= p.nsub) finish_nb(r - 1, nb);
@@ -562,10 +555,14 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
       pend[nb] = acc[nb];
       acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    if (!kDefer) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) finish_nb(r, nb);
+    }
   };
 
   stream_driver<FAST, RESIDENT, RING>(p, tr, Bp, smem, body, round_end);
-  if (tr.rounds > 0) {
+  if (kDefer && tr.rounds > 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) finish_nb(tr.rounds - 1, nb);
   }
@@ -656,12 +653,14 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
     for (int j = 0; j < 8; j += 2) {
 #pragma unroll
       for (int b = 0; b < BD; ++b) h1[b] = *(const u32x4_t*)(hb + b * rs + (j + 1) * 16);
+      __builtin_amdgcn_sched_barrier(0);  // reads of step j + 1 stay ahead of the products of step j
 #pragma unroll
       for (int b = 0; b < BD; ++b) acc[b] = dot8(cur[j], h0[b], acc[b]);
       if (j + 2 < 8) {
 #pragma unroll
         for (int b = 0; b < BD; ++b) h0[b] = *(const u32x4_t*)(hb + b * rs + (j + 2) * 16);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < BD; ++b) acc[b] = dot8(cur[j + 1], h1[b], acc[b]);
     }
