@@ -28,8 +28,9 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/step and achieved HBM GB/s (% of peak) for FMMS at V=151936, B=1–64"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fmms_mid_decode_B64_hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_matmul_amd", "csrc", f) for f in
-                  ("fs_kernels.hip", "fs_device.h", "fs_kernels.h", "fs_api.hip")]
+CSRC = os.path.join(ROOT, "lm_head_matmul_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+CALIB_BYTES = 1 << 30  # the --profile run's plain device fill + copy
 
 
 def parse_args():
@@ -43,6 +44,11 @@ def parse_args():
     ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3: one 1 GiB device copy (counter calibration), then the "
+                         "headline steps only")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the profiles/ summaries from a --profile run's rocprofv3 csv output and exit")
     return ap.parse_args()
 
 
@@ -76,6 +82,81 @@ def measured_traffic():
         return None
 
 
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace "
+             "-- python3 bench.py --profile --steps 1000 --warmup 50",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch "
+             "-- python3 bench.py --profile --steps 5 --warmup 2",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write "
+             "-- python3 bench.py --profile --steps 5 --warmup 2",
+}
+HEADLINE_KERNEL = "fmms_mfma_kernel"
+
+
+def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B=64):
+    """Turn a --profile run's rocprofv3 csv files into the two committed text summaries."""
+    import csv
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    algo = algorithmic_bytes(B, w["d"], w["V"])
+    tag = f"{workload}_B{B}"
+    pre = "cd /tmp && export TMPDIR=/tmp && cd <repo root> && "
+
+    stats = list(csv.DictReader(open(trace_csv)))
+    head = [r for r in stats if HEADLINE_KERNEL in r["Name"]]
+    assert len(head) == 1, "expected one headline kernel instance in the trace"
+    avg_us = float(head[0]["AverageNs"]) / 1e3
+    lines = [f"# {HEADLINE_KERNEL}: {workload} head (B={B}, d={w['d']}, V={w['V']}), kernel trace", "",
+             f"command: `{pre}{PROFILE_CMDS['trace']}`", "",
+             "The run: one 1 GiB device fill and copy (counter calibration), 50 warmup and 1000 timed steps.", "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    lines += ["", f"- headline_kernel_average_us: {avg_us:.2f}",
+              f"- algorithmic_bytes_per_launch: {algo}",
+              f"- achieved_GB_per_s_at_trace_average: {algo / (avg_us * 1e-6) / 1e9:.1f}",
+              f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
+    path = os.path.join(ROOT, "profiles", f"{HEADLINE_KERNEL}_{tag}_kernel_trace.md")
+    open(path, "w").write("\n".join(lines))
+
+    def rows(fn):
+        return list(csv.DictReader(open(fn)))
+
+    def calib(rs, counter):
+        # the fill kernel writes CALIB_BYTES; the copy that follows it reads CALIB_BYTES
+        fill = next(i for i, r in enumerate(rs) if "FillFunctor<short>" in r["Kernel_Name"])
+        copy = next(r for r in rs[fill + 1:] if "copyBuffer" in r["Kernel_Name"])
+        kib = float((rs[fill] if counter == "WRITE_SIZE" else copy)["Counter_Value"])
+        return (CALIB_BYTES / 1024) / kib, kib
+
+    fr, wr = rows(fetch_csv), rows(write_csv)
+    f_fac, f_cal = calib(fr, "FETCH_SIZE")
+    w_fac, w_cal = calib(wr, "WRITE_SIZE")
+    f_k = [float(r["Counter_Value"]) for r in fr if HEADLINE_KERNEL in r["Kernel_Name"]]
+    w_k = [float(r["Counter_Value"]) for r in wr if HEADLINE_KERNEL in r["Kernel_Name"]]
+    f_kib, w_kib = sum(f_k) / len(f_k), sum(w_k) / len(w_k)
+    hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
+    lines = [f"# {HEADLINE_KERNEL}: {workload} head (B={B}, d={w['d']}, V={w['V']}), HBM traffic per launch", "",
+             f"fetch pass: `{pre}{PROFILE_CMDS['fetch']}`", "",
+             f"write pass: `{pre}{PROFILE_CMDS['write']}`", "",
+             "Calibration: the same runs first fill 1 GiB (a pure write) and copy it (a 1 GiB read + write).",
+             f"FETCH_SIZE reads {f_cal:.1f} KiB for the copy's 1048576 KiB read (factor {f_fac:.5f});",
+             f"WRITE_SIZE reads {w_cal:.1f} KiB for the fill's 1048576 KiB write (factor {w_fac:.5f}).",
+             f"Kernel dispatches seen: {len(f_k)} (fetch pass), {len(w_k)} (write pass).", "",
+             f"- fetch_kib_per_launch_raw: {f_kib:.1f}",
+             f"- write_kib_per_launch_raw: {w_kib:.1f}",
+             f"- fetch_scale: {f_fac:.5f}",
+             f"- write_scale: {w_fac:.5f}",
+             f"- hbm_bytes_per_launch: {hbm:.0f}",
+             f"- algorithmic_bytes_per_launch: {algo}",
+             f"- traffic_over_algorithmic: {hbm / algo:.4f}",
+             f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
+    open(TRAFFIC_SUMMARY, "w").write("\n".join(lines))
+    print(f"wrote {path} and {TRAFFIC_SUMMARY}: avg {avg_us:.1f} us, traffic {hbm / algo:.4f} x algorithmic")
+
+
 class Timer:
     """HIP events on the stream the kernels are launched on."""
 
@@ -100,6 +181,9 @@ class Timer:
 
 def main():
     args = parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}),
               flush=True)
@@ -152,6 +236,15 @@ def main():
         ms, wall = timer.run(lambda i: step(i, warmup), steps)
         return ms, wall
 
+    if args.profile:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        dst = src.clone()
+        torch.cuda.synchronize()
+        del src, dst
+        args.no_sweep = True
+        args.no_cpu_baseline = True
+
     # --- headline ---------------------------------------------------------------
     w = synth.WORKLOADS[args.workload]
     B, d, V, T = args.batch, w["d"], w["V"], w["T"]
@@ -160,8 +253,11 @@ def main():
     algo = algorithmic_bytes(B, d, V)
     gbs = algo / (ms * 1e-3) / 1e9
     log(f"headline: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of 8 TB/s), wall {wall:.3f}s")
-    ms_u, _ = time_fmms(args.workload, B, min(args.steps, 200), 10, T, unfused=True)
-    log(f"headline unfused: {ms_u * 1e3:.1f} us/step")
+    if args.profile:
+        ms_u = None
+    else:
+        ms_u, _ = time_fmms(args.workload, B, min(args.steps, 200), 10, T, unfused=True)
+        log(f"headline unfused: {ms_u * 1e3:.1f} us/step")
 
     result = {
         "metric": METRIC,
@@ -179,8 +275,8 @@ def main():
         "config": {"workload": f"{args.workload}_head", "B": B, "d": d, "V": V, "temperature": T, "top_k": 0,
                    "us_per_step": round(ms * 1e3, 2), "rows_per_s": round(B / (ms * 1e-3)),
                    "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-                   "unfused_us_per_step": round(ms_u * 1e3, 2),
-                   "fused_speedup_vs_unfused": round(ms_u / ms, 3)},
+                   "unfused_us_per_step": None if ms_u is None else round(ms_u * 1e3, 2),
+                   "fused_speedup_vs_unfused": None if ms_u is None else round(ms_u / ms, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": algo},
@@ -254,17 +350,18 @@ def main():
         cores = oracle.num_threads()
         rows_done, t_used = 0, 0.0
         t0 = time.perf_counter()
-        while t_used < args.cpu_seconds and rows_done < B * 4:
-            r = min(8, B)
-            oracle.fmms_sample(Hh[:r], Wh, T, 0, rows_done)
+        r = min(8, B)
+        while t_used < args.cpu_seconds and rows_done < B:
+            oracle.fmms_sample(Hh[rows_done:rows_done + r], Wh, T, 0, 0)
             rows_done += r
             t_used = time.perf_counter() - t0
         per_step = t_used / rows_done * B  # the oracle's cost is linear in the rows it samples
         cpu_gbs = algo / per_step / 1e9
+        sample = (f"{rows_done} of the {B} rows of one step (full V={V}, d={d}: fp64 logits, noise, argmax) "
+                  f"in {t_used:.1f}s" + ("" if rows_done == B else f"; step time scaled by {B}/{rows_done}"))
         result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                                  "sample": f"{rows_done} of the {B} rows (full V={V}, d={d}: logits, noise, "
-                                            f"argmax) in {t_used:.1f}s; per-step time scaled by {B}/{rows_done}",
-                                  "seconds_per_step": round(per_step, 3)}
+                                  "sample": sample, "seconds_per_step": round(per_step, 3),
+                                  "us_per_step": round(per_step * 1e6, 1)}
         log(f"cpu baseline {result['cpu_baseline']}")
 
     fs.fs_destroy(ctx)

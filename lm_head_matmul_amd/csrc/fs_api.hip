@@ -81,7 +81,9 @@ int pow2_at_least(int x) {
 
 // Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB).
 int choose_config(int B, int path, fsk::StreamConfig& cfg) {
-  const int dot_max = env_int("FS_DOT_MAX_B", fsk::kDotMaxB);
+  // AUTO takes the MFMA kernel at every batch size: on gfx950 it streams W
+  // faster than the dot-product kernel even at B = 1 (measured).
+  const int dot_max = env_int("FS_DOT_MAX_B", 0);
   bool dot;
   if (path == FS_PATH_DOT) {
     if (B > fsk::kDotMaxB) return fail(FS_ERR_UNSUPPORTED, "dot-product path supports B <= %d (got %d)", fsk::kDotMaxB, B);
