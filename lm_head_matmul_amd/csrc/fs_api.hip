@@ -20,18 +20,15 @@ struct fs_ctx {
   int max_top_k;
   int n_cu;
   int max_tiles;
-  // [max_B][max_tiles] per-tile winners (and log-sum-exp state), plus tickets
+  // [max_B][max_tiles] per-tile winners (and log-sum-exp state)
   float* ws_val;
   int32_t* ws_idx;
   float* ws_m;
   float* ws_s;
-  unsigned int* tickets;  // one per kernel family, zero between launches
   void* base;
 };
 
 namespace {
-
-enum { TICKET_STREAM = 0, TICKET_SAMPLE = 1, N_TICKETS = 4 };
 
 thread_local std::string g_error;
 
@@ -152,17 +149,23 @@ void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int
   p.ws_idx = ctx->ws_idx;
   p.ws_m = ctx->ws_m;
   p.ws_s = ctx->ws_s;
-  p.ticket = ctx->tickets + TICKET_STREAM;
 }
 
 // Launches the streaming kernel over the batch in chunks of at most
-// kMfmaMaxB rows (each chunk streams W once).  `per_chunk` adjusts the output
-// pointers of a chunk that starts at batch row r0.
+// kMfmaMaxB rows (each chunk streams W once); with a mask, chunks are also
+// small enough for their tile masks to fit the LDS staging area.  `per_chunk`
+// adjusts the output pointers of a chunk that starts at batch row r0.
 template <typename F>
 int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk) {
   const int B = base.B;
-  for (int r0 = 0; r0 < B; r0 += fsk::kMfmaMaxB) {
-    const int Bc = (B - r0) < fsk::kMfmaMaxB ? (B - r0) : fsk::kMfmaMaxB;
+  int chunk = fsk::kMfmaMaxB;
+  if (base.mask) {
+    const int64_t rows = fsk::kMaskLdsMax / (4 * fsk::tile_mask_words(base.n_mblocks, base.n_tiles));
+    if (rows < 1) return fail(FS_ERR_UNSUPPORTED, "V=%lld: a tile's mask does not fit the LDS staging area", (long long)base.V);
+    if (rows < chunk) chunk = (int)rows;
+  }
+  for (int r0 = 0; r0 < B; r0 += chunk) {
+    const int Bc = (B - r0) < chunk ? (B - r0) : chunk;
     fsk::StreamParams p = base;
     p.B = Bc;
     p.H = base.H + (int64_t)r0 * base.ldh;
@@ -210,15 +213,13 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
   }
   c->max_tiles = c->n_cu;
   const size_t n = (size_t)max_B * (size_t)c->max_tiles;
-  const size_t bytes = 4 * n * sizeof(float) + N_TICKETS * sizeof(unsigned int) + 256;
+  const size_t bytes = 4 * n * sizeof(float) + 256;
   e = hipMalloc(&c->base, bytes);
   if (e != hipSuccess) {
     delete c;
     return hip_fail(e, "hipMalloc(workspace)");
   }
   char* b = (char*)c->base;
-  c->tickets = (unsigned int*)b;
-  b += 256;
   c->ws_val = (float*)b;
   c->ws_idx = (int32_t*)(c->ws_val + n);
   c->ws_m = (float*)(c->ws_idx + n);
@@ -298,7 +299,7 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
   hipStream_t s = (hipStream_t)stream;
   fsk::StreamParams p;
-  fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
+  fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, nullptr, 0);  // the GEMM pass ignores the mask
   rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
     c.logits = logits_ws + (int64_t)r0 * ldl;
     c.ldl = ldl;
@@ -320,7 +321,6 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   q.n_tiles = n_tiles_for(ctx, V);
   q.ws_val = ctx->ws_val;
   q.ws_idx = ctx->ws_idx;
-  q.ticket = ctx->tickets + TICKET_SAMPLE;
   q.out_idx = out_idx;
   hipError_t e = fsk::launch_sample_logits(q, s);
   if (e != hipSuccess) return hip_fail(e, "sampling kernel launch");

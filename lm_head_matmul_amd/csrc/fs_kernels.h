@@ -36,14 +36,13 @@ struct StreamParams {
   int nchunk;         // ceil(nsub / cs)
   int nbuf;           // LDS buffers for H chunks (1 or 2)
   int h_rowstride;    // bytes per H row in LDS
-  int mask_words;     // mask words per row staged in LDS (0: read the mask from global memory)
+  int mask_words;     // mask words per row staged in LDS (set whenever mask is non-null)
   int mask_lds_off;   // byte offset of the staged mask in LDS
   // per-tile results, [B][n_tiles]
   float* ws_val;
   int32_t* ws_idx;
   float* ws_m;
   float* ws_s;
-  unsigned int* ticket;  // zero between launches; the last workgroup resets it
   int32_t* out_idx;
   GroupSummary* out_sum;
   float* dbg_max;  // [B][n_tiles] or null
@@ -64,7 +63,6 @@ struct SampleParams {  // unfused second pass: sample from stored logits
   int n_tiles;
   float* ws_val;
   int32_t* ws_idx;
-  unsigned int* ticket;
   int32_t* out_idx;
 };
 
@@ -85,6 +83,12 @@ constexpr int kDotMaxB = 2;
 constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
 constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
+constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
+
+// Mask words per row staged for the largest tile of a launch.
+inline int64_t tile_mask_words(int64_t n_mblocks, int n_tiles) {
+  return 16 * ((n_mblocks + n_tiles - 1) / n_tiles) / 32 + 2;
+}
 
 // Fills the K/LDS geometry fields of p and the LDS size of cfg; returns false
 // if the shape does not fit the kernels' LDS budget.

@@ -61,7 +61,6 @@ __global__ void __launch_bounds__(kThreads) sample_logits_kernel(const SamplePar
       p.ws_idx[(int64_t)b * p.n_tiles + t] = bi;
     }
   }
-  finish_tiles<EPI_FLAT>(p.B, p.n_tiles, p.ws_val, p.ws_idx, nullptr, nullptr, p.ticket, p.out_idx, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -179,16 +178,13 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg) {
   auto rowstride = [](int cs) { return cs * 512 + 16; };
   // mask words of the largest tile (tile rows are a whole number of 16-row blocks)
   int mask_bytes = 0;
+  p.mask_words = 0;
   if (p.mask) {
-    const int64_t max_rows = 16 * ((p.n_mblocks + p.n_tiles - 1) / p.n_tiles);
-    const int64_t words = max_rows / 32 + 2;
+    const int64_t words = tile_mask_words(p.n_mblocks, p.n_tiles);
     const int64_t bytes = ((int64_t)p.B * words * 4 + 15) / 16 * 16;
-    if (bytes <= 16 * 1024) {
-      p.mask_words = (int)words;
-      mask_bytes = (int)bytes;
-    } else {
-      p.mask_words = 0;
-    }
+    if (bytes > kMaskLdsMax) return false;
+    p.mask_words = (int)words;
+    mask_bytes = (int)bytes;
   }
   const int budget = kLdsMax - mask_bytes;
   if ((int64_t)Bp * rowstride(p.nsub) <= budget) {  // whole H resident
@@ -234,10 +230,23 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg) {
   return true;
 }
 
+// The streaming pass, then (sampling epilogues) the reduction over its tiles.
 hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream) {
+  hipError_t e;
+  const dim3 rgrid((p.B + kWaves - 1) / kWaves);
   switch (epi) {
-    case EPI_FLAT: return launch_stream_epi<EPI_FLAT>(p, cfg, stream);
-    case EPI_GROUP: return launch_stream_epi<EPI_GROUP>(p, cfg, stream);
+    case EPI_FLAT:
+      e = launch_stream_epi<EPI_FLAT>(p, cfg, stream);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_tiles_kernel<EPI_FLAT>, rgrid, dim3(kThreads), 0, stream, p.B, p.n_tiles, p.ws_val,
+                         p.ws_idx, nullptr, nullptr, p.out_idx, nullptr);
+      return hipGetLastError();
+    case EPI_GROUP:
+      e = launch_stream_epi<EPI_GROUP>(p, cfg, stream);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(reduce_tiles_kernel<EPI_GROUP>, rgrid, dim3(kThreads), 0, stream, p.B, p.n_tiles, p.ws_val,
+                         p.ws_idx, p.ws_m, p.ws_s, nullptr, p.out_sum);
+      return hipGetLastError();
     case EPI_STORE: return launch_stream_epi<EPI_STORE>(p, cfg, stream);
     default: return hipErrorInvalidValue;
   }
@@ -245,6 +254,10 @@ hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi
 
 hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(sample_logits_kernel, dim3(p.n_tiles), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_tiles_kernel<EPI_FLAT>, dim3((p.B + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, p.B,
+                     p.n_tiles, p.ws_val, p.ws_idx, nullptr, nullptr, p.out_idx, nullptr);
   return hipGetLastError();
 }
 

@@ -21,8 +21,8 @@
 //    reads of 16 lanes land in distinct banks.
 //  * Epilogue per round, on the accumulators: scale by 1/T, mask, Philox4x32-10
 //    noise (one call covers the four consecutive vocab ids a lane holds), argmax
-//    update.  Per tile, the winners go to a [B, n_tiles] workspace; the last
-//    workgroup to finish (device-scope ticket) reduces over tiles.
+//    update.  Per tile, the winners go to a [B, n_tiles] workspace, which a
+//    second small launch on the same stream reduces over tiles.
 #pragma once
 
 #include <atomic>
@@ -33,61 +33,49 @@
 namespace fsk {
 
 // ---------------------------------------------------------------------------
-// Cross-tile reduction by the last workgroup to finish.
+// Cross-tile reduction: a second, small launch on the same stream (the kernel
+// boundary publishes the workspace), one wave per batch row over its n_tiles
+// entries.  [FlashSampling, arXiv 2603.15854, section 3: the stage-2 reduction
+// over tiles]
 // ---------------------------------------------------------------------------
 template <int EPI>
-__device__ void finish_tiles(const int B, const int n_tiles, const float* __restrict__ ws_val,
-                             const int32_t* __restrict__ ws_idx, const float* __restrict__ ws_m,
-                             const float* __restrict__ ws_s, unsigned int* ticket, int32_t* out_idx,
-                             GroupSummary* out_sum) {
-  // Publication protocol: the barrier orders every thread's workspace stores
-  // before thread 0's device-scope release increment; only the workgroup that
-  // takes the last ticket performs the matching device-scope acquire.  (An
-  // acquire in every workgroup would invalidate each XCD's L2 under the
-  // workgroups still streaming W.)
-  __shared__ int s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(n_tiles - 1));
+__global__ void __launch_bounds__(kThreads)
+    reduce_tiles_kernel(const int B, const int n_tiles, const float* __restrict__ ws_val,
+                        const int32_t* __restrict__ ws_idx, const float* __restrict__ ws_m,
+                        const float* __restrict__ ws_s, int32_t* __restrict__ out_idx,
+                        GroupSummary* __restrict__ out_sum) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (b >= B) return;
+  float v = -INFINITY, m = -INFINITY, s = 0.0f;
+  int32_t i = -1;
+  for (int t = lane; t < n_tiles; t += 64) {
+    const int64_t o = (int64_t)b * n_tiles + t;
+    merge_best(v, i, ws_val[o], ws_idx[o]);
+    if (EPI == EPI_GROUP) lse_merge(m, s, ws_m[o], ws_s[o]);
   }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int b = wave; b < B; b += kWaves) {
-    float v = -INFINITY, m = -INFINITY, s = 0.0f;
-    int32_t i = -1;
-    for (int t = lane; t < n_tiles; t += 64) {
-      const int64_t o = (int64_t)b * n_tiles + t;
-      merge_best(v, i, ws_val[o], ws_idx[o]);
-      if (EPI == EPI_GROUP) lse_merge(m, s, ws_m[o], ws_s[o]);
-    }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(v, off);
-      const int32_t oi = __shfl_xor(i, off);
-      merge_best(v, i, ov, oi);
-      if (EPI == EPI_GROUP) {
-        const float om = __shfl_xor(m, off);
-        const float os = __shfl_xor(s, off);
-        lse_merge(m, s, om, os);
-      }
-    }
-    if (lane == 0) {
-      if (EPI == EPI_GROUP) {
-        GroupSummary g;
-        g.lse = (m == -INFINITY) ? -INFINITY : m + logf(s);
-        g.pmax = v;
-        g.arg = i;
-        out_sum[b] = g;
-      } else {
-        out_idx[b] = i;
-      }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int32_t oi = __shfl_xor(i, off);
+    merge_best(v, i, ov, oi);
+    if (EPI == EPI_GROUP) {
+      const float om = __shfl_xor(m, off);
+      const float os = __shfl_xor(s, off);
+      lse_merge(m, s, om, os);
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) {
+    if (EPI == EPI_GROUP) {
+      GroupSummary g;
+      g.lse = (m == -INFINITY) ? -INFINITY : m + logf(s);
+      g.pmax = v;
+      g.arg = i;
+      out_sum[b] = g;
+    } else {
+      out_idx[b] = i;
+    }
+  }
 }
 
 // Per-wave results (already reduced inside the wave) sit in LDS scratch as
@@ -160,12 +148,25 @@ __device__ __forceinline__ void h_store(const StreamParams& p, unsigned char* bu
   *(u32x4_t*)(buf + n * p.h_rowstride + q * 16) = v;
 }
 
-// Stages the whole chunk (all pieces) directly.
+// Stages the whole chunk at kernel start: rows >= B are zero-filled without
+// loads; the valid rows go in batches of kMaxStagePieces loads per thread, so
+// a thread waits once per batch rather than once per piece.
 __device__ void h_stage_all(const StreamParams& p, int Bp, int cidx, unsigned char* buf) {
-  const int np = Bp * p.cs * 32;
-  for (int P = threadIdx.x; P < np; P += kThreads) {
-    const u32x4_t v = h_load(p, cidx, P);
-    h_store(p, buf, P, h_valid(p, cidx, P) ? v : u32x4_t{0u, 0u, 0u, 0u});
+  const int per_row = p.cs * 32;
+  const int nv = p.B * per_row, np = Bp * per_row;
+  for (int P = nv + threadIdx.x; P < np; P += kThreads) h_store(p, buf, P, u32x4_t{0u, 0u, 0u, 0u});
+  for (int P0 = 0; P0 < nv; P0 += kMaxStagePieces * kThreads) {
+    u32x4_t v[kMaxStagePieces];
+#pragma unroll
+    for (int i = 0; i < kMaxStagePieces; ++i) {
+      const int P = P0 + threadIdx.x + i * kThreads;
+      v[i] = h_load(p, cidx, P < nv ? P : nv - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxStagePieces; ++i) {
+      const int P = P0 + threadIdx.x + i * kThreads;
+      if (P < nv) h_store(p, buf, P, h_valid(p, cidx, P) ? v[i] : u32x4_t{0u, 0u, 0u, 0u});
+    }
   }
 }
 
@@ -190,24 +191,39 @@ __device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], c
   }
 }
 
-// The vocabulary mask of the tile, staged in LDS at kernel start (when it fits,
-// p.mask_words > 0): rows b < B, words [w_lo, w_lo + p.mask_words) of each row.
-// Reading mask bits from LDS keeps global loads out of the epilogue: the
-// vector-memory counter is in order, so waiting for one mask word would also
-// wait for every W prefetch issued before it.
+// The vocabulary mask of the tile, staged in LDS at kernel start: rows b < B,
+// words [w_lo, w_lo + p.mask_words) of each row (the host sizes batch chunks so
+// that it always fits).  Reading mask bits from LDS keeps global loads out of
+// the epilogue: the vector-memory counter is in order, so waiting for one mask
+// word would also wait for every W prefetch issued before it.
 __device__ __forceinline__ int64_t mask_w_lo(const StreamParams& p, const TileRange& tr) {
   return (p.vocab_offset + tr.mb_lo * 16) >> 5;
 }
 
 __device__ void mask_stage(const StreamParams& p, const TileRange& tr, uint32_t* lds) {
-  if (!p.mask || p.mask_words == 0) return;
+  if (!p.mask) return;
   const int64_t w_lo = mask_w_lo(p, tr);
   const int64_t w_max = (p.vocab_offset + p.V - 1) >> 5;  // last word of the launch's vocabulary
   const int n = p.B * p.mask_words;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int b = i / p.mask_words;
-    const int64_t w = w_lo + (i - b * p.mask_words);
-    lds[i] = w <= w_max ? p.mask[((int64_t)p.row_offset + b) * p.ldm + w] : 0u;
+  for (int i0 = 0; i0 < n; i0 += 4 * kThreads) {
+    uint32_t w4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + threadIdx.x + j * kThreads;
+      const int ii = i < n ? i : n - 1;
+      const int b = ii / p.mask_words;
+      int64_t w = w_lo + (ii - b * p.mask_words);
+      w = w <= w_max ? w : w_max;
+      w4[j] = p.mask[((int64_t)p.row_offset + b) * p.ldm + w];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + threadIdx.x + j * kThreads;
+      if (i < n) {
+        const int b = i / p.mask_words;
+        lds[i] = (w_lo + (i - b * p.mask_words) <= w_max) ? w4[j] : 0u;
+      }
+    }
   }
 }
 
@@ -215,11 +231,7 @@ __device__ void mask_stage(const StreamParams& p, const TileRange& tr, uint32_t*
 __device__ __forceinline__ uint32_t mask_bits4(const StreamParams& p, const uint32_t* lds, int64_t w_lo, int64_t gv0,
                                                int b) {
   if (!p.mask) return 0xFu;
-  uint32_t word;
-  if (p.mask_words > 0)
-    word = lds[b * p.mask_words + (int)((gv0 >> 5) - w_lo)];
-  else
-    word = p.mask[((int64_t)p.row_offset + b) * p.ldm + (gv0 >> 5)];
+  const uint32_t word = lds[b * p.mask_words + (int)((gv0 >> 5) - w_lo)];
   return (word >> (uint32_t)(gv0 & 31)) & 0xFu;
 }
 
@@ -600,7 +612,6 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   }
   __syncthreads();
   publish_tile<EPI>(p, Bp, sv, si, sm, ss);
-  finish_tiles<EPI>(p.B, p.n_tiles, p.ws_val, p.ws_idx, p.ws_m, p.ws_s, p.ticket, p.out_idx, p.out_sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -738,7 +749,6 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
   }
   __syncthreads();
   publish_tile<EPI>(p, BD, sv, si, sm, ss);
-  finish_tiles<EPI>(p.B, p.n_tiles, p.ws_val, p.ws_idx, p.ws_m, p.ws_s, p.ticket, p.out_idx, p.out_sum);
 }
 
 // ---------------------------------------------------------------------------
