@@ -174,7 +174,7 @@ int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t str
     fsk::StreamConfig cfg;
     int rc = choose_config(Bc, path, cfg);
     if (rc != FS_OK) return rc;
-    if (!fsk::plan_stream(p, cfg))
+    if (!fsk::plan_stream(p, cfg, epi))
       return fail(FS_ERR_UNSUPPORTED, "shape B=%d d=%d does not fit the LDS budget", Bc, p.d);
     hipError_t e = fsk::launch_stream(p, cfg, epi, stream);
     if (e != hipSuccess) return hip_fail(e, "streaming kernel launch");

@@ -23,6 +23,10 @@ constexpr int kWave = 64;
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64-bit multiplies and xors; the key advances by a Weyl step after each
 // round.  One call yields the four words of four consecutive vocab ids.
+// The products are formed as separate high and low 32-bit multiplies: the
+// fused 64-bit form (v_mad_u64_u32 with a scalar operand, which writes a carry
+// to scalar registers) stalled the W stream measurably on gfx950, the split
+// form does not.
 // ---------------------------------------------------------------------------
 struct Philox4 {
   uint32_t w[4];
@@ -32,12 +36,12 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t k0, uint32_t k1, uint3
                                                  uint32_t c3) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c0;
-    const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
-    const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
-    c1 = (uint32_t)pb;
-    c3 = (uint32_t)pa;
+    const uint32_t hi_a = __umulhi(0xD2511F53u, c0), lo_a = 0xD2511F53u * c0;
+    const uint32_t hi_b = __umulhi(0xCD9E8D57u, c2), lo_b = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi_b ^ c1 ^ k0;
+    const uint32_t n2 = hi_a ^ c3 ^ k1;
+    c1 = lo_b;
+    c3 = lo_a;
     c0 = n0;
     c2 = n2;
     k0 += 0x9E3779B9u;

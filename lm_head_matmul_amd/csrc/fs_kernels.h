@@ -36,6 +36,10 @@ struct StreamParams {
   int nchunk;         // ceil(nsub / cs)
   int nbuf;           // LDS buffers for H chunks (1 or 2)
   int h_rowstride;    // bytes per H row in LDS
+  int h_rows;         // H rows per LDS buffer: the B rows of H, plus one zero row read by the
+                      // padding lanes of a 16-wide MFMA block when B is not a multiple of 16
+  int noise_pitch;    // > 0: the tile's Gumbel noise is precomputed into LDS, this many floats per row
+  int noise_lds_off;  // byte offset of the noise table in LDS
   int mask_words;     // mask words per row staged in LDS (set whenever mask is non-null)
   int mask_lds_off;   // byte offset of the staged mask in LDS
   // per-tile results, [B][n_tiles]
@@ -92,7 +96,7 @@ inline int64_t tile_mask_words(int64_t n_mblocks, int n_tiles) {
 
 // Fills the K/LDS geometry fields of p and the LDS size of cfg; returns false
 // if the shape does not fit the kernels' LDS budget.
-bool plan_stream(StreamParams& p, StreamConfig& cfg);
+bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi);
 
 hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream);
 template <int EPI>

@@ -171,11 +171,14 @@ __global__ void debug_gumbel_scan_init(unsigned long long* stats) {
 // LDS plan of a streaming launch: H resident when it fits (after the mask),
 // else k-chunks (double-buffered when two fit); the tile's mask words are
 // staged when they fit beside H.  Prefers the layouts the fast driver takes.
-bool plan_stream(StreamParams& p, StreamConfig& cfg) {
+bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   const int Bp = cfg.dot ? cfg.bd : cfg.nb * 16;
+  const int hr = cfg.dot ? cfg.bd : (p.B < Bp ? p.B + 1 : Bp);
+  p.h_rows = hr;
   p.nsub = (p.d + 255) / 256;
   const int scratch = kWaves * Bp * 16;
   auto rowstride = [](int cs) { return cs * 512 + 16; };
+  const int64_t tile_rows = 16 * ((p.n_mblocks + p.n_tiles - 1) / p.n_tiles);  // largest tile
   // mask words of the largest tile (tile rows are a whole number of 16-row blocks)
   int mask_bytes = 0;
   p.mask_words = 0;
@@ -187,14 +190,14 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg) {
     mask_bytes = (int)bytes;
   }
   const int budget = kLdsMax - mask_bytes;
-  if ((int64_t)Bp * rowstride(p.nsub) <= budget) {  // whole H resident
+  if ((int64_t)hr * rowstride(p.nsub) <= budget) {  // whole H resident
     p.cs = p.nsub;
     p.nchunk = 1;
     p.nbuf = 1;
   } else {
     int cs = 0;
     auto fits2 = [&](int c) {
-      return (int64_t)2 * Bp * rowstride(c) <= budget && Bp * c * 32 <= kMaxStagePieces * kThreads;
+      return (int64_t)2 * hr * rowstride(c) <= budget && hr * c * 32 <= kMaxStagePieces * kThreads;
     };
     if (p.nsub % kFastRingChunked == 0 && fits2(kFastRingChunked)) {
       cs = kFastRingChunked;
@@ -208,7 +211,7 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg) {
     if (cs > 0) {
       p.cs = cs;
       p.nbuf = 2;
-    } else if ((int64_t)Bp * rowstride(1) <= budget && Bp * 32 <= kMaxStagePieces * kThreads) {
+    } else if ((int64_t)hr * rowstride(1) <= budget && hr * 32 <= kMaxStagePieces * kThreads) {
       p.cs = 1;
       p.nbuf = 1;
     } else {
@@ -218,15 +221,29 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg) {
     if (p.nchunk == 1) p.nbuf = 1;
   }
   p.h_rowstride = rowstride(p.cs);
-  const int hbytes = p.nbuf * Bp * p.h_rowstride;
+  const int hbytes = p.nbuf * hr * p.h_rowstride;
   p.mask_lds_off = hbytes;
-  const int total = hbytes + mask_bytes;
-  cfg.lds_bytes = total > scratch ? total : scratch;
+  int total = hbytes + mask_bytes;
+  // Noise table: the tile's Gumbel noise for the B rows, computed before the
+  // stream starts (every lane does useful work there, while in the epilogue a
+  // 16-row MFMA block with B < 16 would compute noise for padding rows).
+  p.noise_pitch = 0;
+  p.noise_lds_off = 0;
   const bool full_k = p.d % 256 == 0;
   if (p.nchunk == 1)
     cfg.fast = full_k && p.nsub % kFastRingResident == 0;
   else
     cfg.fast = full_k && p.cs == kFastRingChunked && p.nbuf == 2 && p.nsub % kFastRingChunked == 0;
+  if (!cfg.dot && cfg.fast && epi != EPI_STORE) {
+    const int pitch = (int)tile_rows + 4;
+    const int64_t nbytes = (int64_t)p.B * pitch * 4;
+    if (total + nbytes <= kLdsMax) {
+      p.noise_pitch = pitch;
+      p.noise_lds_off = total;
+      total += (int)nbytes;
+    }
+  }
+  cfg.lds_bytes = total > scratch ? total : scratch;
   return true;
 }
 

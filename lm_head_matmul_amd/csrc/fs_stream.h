@@ -151,9 +151,9 @@ __device__ __forceinline__ void h_store(const StreamParams& p, unsigned char* bu
 // Stages the whole chunk at kernel start: rows >= B are zero-filled without
 // loads; the valid rows go in batches of kMaxStagePieces loads per thread, so
 // a thread waits once per batch rather than once per piece.
-__device__ void h_stage_all(const StreamParams& p, int Bp, int cidx, unsigned char* buf) {
+__device__ void h_stage_all(const StreamParams& p, int cidx, unsigned char* buf) {
   const int per_row = p.cs * 32;
-  const int nv = p.B * per_row, np = Bp * per_row;
+  const int nv = p.B * per_row, np = p.h_rows * per_row;
   for (int P = nv + threadIdx.x; P < np; P += kThreads) h_store(p, buf, P, u32x4_t{0u, 0u, 0u, 0u});
   for (int P0 = 0; P0 < nv; P0 += kMaxStagePieces * kThreads) {
     u32x4_t v[kMaxStagePieces];
@@ -172,8 +172,8 @@ __device__ void h_stage_all(const StreamParams& p, int Bp, int cidx, unsigned ch
 
 // Prefetch of the next chunk into registers: raw, unconditional loads (so the
 // W stream in flight is never drained by a wait); masking happens at commit.
-__device__ __forceinline__ void h_prefetch(u32x4_t (&hs)[kMaxStagePieces], const StreamParams& p, int Bp, int cidx) {
-  const int np = Bp * p.cs * 32;
+__device__ __forceinline__ void h_prefetch(u32x4_t (&hs)[kMaxStagePieces], const StreamParams& p, int cidx) {
+  const int np = p.h_rows * p.cs * 32;
 #pragma unroll
   for (int i = 0; i < kMaxStagePieces; ++i) {
     const int P = threadIdx.x + i * kThreads;
@@ -181,9 +181,9 @@ __device__ __forceinline__ void h_prefetch(u32x4_t (&hs)[kMaxStagePieces], const
   }
 }
 
-__device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], const StreamParams& p, int Bp, int cidx,
+__device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], const StreamParams& p, int cidx,
                                          unsigned char* buf) {
-  const int np = Bp * p.cs * 32;
+  const int np = p.h_rows * p.cs * 32;
 #pragma unroll
   for (int i = 0; i < kMaxStagePieces; ++i) {
     const int P = threadIdx.x + i * kThreads;
@@ -228,9 +228,11 @@ __device__ void mask_stage(const StreamParams& p, const TileRange& tr, uint32_t*
 }
 
 // Four mask bits of vocab ids gv0 .. gv0+3 (gv0 % 4 == 0) of local row b.
+// Kernels without a mask are compiled with MASKED = false: no mask code at all.
+template <bool MASKED>
 __device__ __forceinline__ uint32_t mask_bits4(const StreamParams& p, const uint32_t* lds, int64_t w_lo, int64_t gv0,
                                                int b) {
-  if (!p.mask) return 0xFu;
+  if (!MASKED) return 0xFu;
   const uint32_t word = lds[b * p.mask_words + (int)((gv0 >> 5) - w_lo)];
   return (word >> (uint32_t)(gv0 & 31)) & 0xFu;
 }
@@ -240,20 +242,48 @@ __device__ __forceinline__ uint32_t mask_bits4(const StreamParams& p, const uint
 // running maximizer (and the log-sum-exp state in grouped mode).  The scan
 // order of a lane is increasing in v, so a strict comparison keeps the lowest
 // id on ties.
+// Gumbel noise of the four consecutive vocab ids gv0 .. gv0+3 (gv0 % 4 == 0,
+// global ids) of global batch row `row`: one Philox call.
+__device__ __forceinline__ f32x4_t noise_quad(const StreamParams& p, int gv0, uint32_t row) {
+  const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)gv0 >> 2, row, p.step_lo, p.step_hi);
+  return f32x4_t{gumbel_from_bits(r.w[0]), gumbel_from_bits(r.w[1]), gumbel_from_bits(r.w[2]),
+                 gumbel_from_bits(r.w[3])};
+}
+
+// The tile's noise table in LDS (when planned, p.noise_pitch > 0): rows b < B,
+// one float per vocab id of the tile, written by all threads before the stream
+// starts (made visible by the driver's first barrier).
+__device__ void noise_stage(const StreamParams& p, const TileRange& tr, float* lds) {
+  const int quads = (int)(tr.mb_hi - tr.mb_lo) * 4;
+  const int n = p.B * quads;
+  const int v_base = (int)p.vocab_offset + (int)(tr.mb_lo * 16);
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int b = i / quads;
+    const int q = i - b * quads;
+    *(f32x4_t*)(lds + b * p.noise_pitch + q * 4) = noise_quad(p, v_base + q * 4, (uint32_t)(p.row_offset + b));
+  }
+}
+
+// Perturbed scores of the four consecutive vocab ids v0 .. v0+3 (local ids,
+// v0 % 4 == 0) given their raw logits, noise and mask bits; updates the
+// running maximizer (and the log-sum-exp state in grouped mode).  The scan
+// order of a lane is increasing in v, so a strict comparison keeps the lowest
+// id on ties.  Vocabulary ids are below 2^31 (checked by the API), so the
+// epilogue works in 32-bit integers.
 template <int EPI>
-__device__ __forceinline__ void epilogue_quad(const StreamParams& p, int64_t v0, int b, const float (&acc)[4],
+__device__ __forceinline__ void epilogue_quad(const StreamParams& p, int v0, const float (&acc)[4], const f32x4_t g,
                                               uint32_t bits, float& bv, int32_t& bi, float& lm, float& ls) {
-  const int64_t gv0 = p.vocab_offset + v0;
-  const int64_t grow = (int64_t)p.row_offset + b;
-  const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)(gv0 >> 2), (uint32_t)grow, p.step_lo, p.step_hi);
+  const int gv0 = (int)p.vocab_offset + v0;
+  const int rem = (int)p.V - v0;
+  const uint32_t ok4 = bits & (rem >= 4 ? 0xFu : (rem <= 0 ? 0u : (1u << rem) - 1u));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool ok = (v0 + i < p.V) && ((bits >> i) & 1u);
+    const bool ok = (ok4 >> i) & 1u;
     const float s = acc[i] * p.inv_t;
-    const float pv = ok ? s + gumbel_from_bits(r.w[i]) : -INFINITY;
+    const float pv = ok ? s + g[i] : -INFINITY;
     if (pv > bv) {
       bv = pv;
-      bi = (int32_t)(gv0 + i);
+      bi = gv0 + i;
     }
     if (EPI == EPI_GROUP && ok) lse_push(lm, ls, s);
   }
@@ -283,12 +313,12 @@ __device__ __forceinline__ const uint16_t* w_row(const StreamParams& p, const Ti
 // compiler's wait counters stay exact and no prefetch is ever drained.
 // ---------------------------------------------------------------------------
 template <int U, bool RESIDENT, class Body, class RoundEnd>
-__device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const TileRange& tr, int Bp,
-                                                   unsigned char* smem, Body&& body, RoundEnd&& round_end) {
+__device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const TileRange& tr, unsigned char* smem,
+                                                   Body&& body, RoundEnd&& round_end) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int nsub = p.nsub, ngrp = nsub / U;
-  const int bufbytes = Bp * p.h_rowstride;
+  const int bufbytes = p.h_rows * p.h_rowstride;
   if (tr.rounds == 0) return;
 
   auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
@@ -311,10 +341,10 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
 
   u32x4_t hs[kMaxStagePieces];
   if (RESIDENT) {
-    h_stage_all(p, Bp, 0, smem);
+    h_stage_all(p, 0, smem);
   } else {
-    h_prefetch(hs, p, Bp, 0);
-    h_commit(hs, p, Bp, 0, smem);
+    h_prefetch(hs, p, 0);
+    h_commit(hs, p, 0, smem);
   }
   __syncthreads();
 
@@ -333,7 +363,7 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
         advance();
         // the chunk after this one (chunk index == group index); past the last
         // group of the last round this stages an unused copy of chunk 0
-        if (!RESIDENT && k == 0) h_prefetch(hs, p, Bp, g + 1 < ngrp ? g + 1 : 0);
+        if (!RESIDENT && k == 0) h_prefetch(hs, p, g + 1 < ngrp ? g + 1 : 0);
         // keep the loads above ahead of the compute below: the scheduler would
         // otherwise sink them under the MFMAs to save registers
         __builtin_amdgcn_sched_barrier(0);
@@ -342,7 +372,7 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
         else
           body(buf[k], smem + (cc & 1) * bufbytes, k, r, g * U + k);
         if (!RESIDENT && k == U - 1) {
-          h_commit(hs, p, Bp, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
+          h_commit(hs, p, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
           __syncthreads();
           ++cc;
         }
@@ -356,14 +386,14 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
 // zeros in the staged H), any chunking, two register buffers.  Conditions are
 // evaluated per sub-block.
 template <bool RESIDENT, class Body, class RoundEnd>
-__device__ __forceinline__ void stream_driver_general(const StreamParams& p, const TileRange& tr, int Bp,
-                                                      unsigned char* smem, Body&& body, RoundEnd&& round_end) {
+__device__ __forceinline__ void stream_driver_general(const StreamParams& p, const TileRange& tr, unsigned char* smem,
+                                                      Body&& body, RoundEnd&& round_end) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int nsub = p.nsub, d = p.d;
   const int cs = RESIDENT ? nsub : p.cs;
   const int nchunk = RESIDENT ? 1 : p.nchunk;
-  const int bufbytes = Bp * p.h_rowstride;
+  const int bufbytes = p.h_rows * p.h_rowstride;
   if (tr.rounds == 0) return;
 
   auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
@@ -377,10 +407,10 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
 
   u32x4_t hs[kMaxStagePieces];
   if (RESIDENT) {
-    h_stage_all(p, Bp, 0, smem);
+    h_stage_all(p, 0, smem);
   } else {
-    h_prefetch(hs, p, Bp, 0);
-    h_commit(hs, p, Bp, 0, smem);
+    h_prefetch(hs, p, 0);
+    h_commit(hs, p, 0, smem);
   }
   __syncthreads();
 
@@ -410,16 +440,16 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
       const bool chunk_end = (sbc == cs - 1 || sb == nsub - 1);
       const bool last_chunk = (r == tr.rounds - 1) && (cidx == nchunk - 1);
       const int next_c = cidx + 1 < nchunk ? cidx + 1 : 0;
-      if (sbc == 0 && !last_chunk) h_prefetch(hs, p, Bp, next_c);
+      if (sbc == 0 && !last_chunk) h_prefetch(hs, p, next_c);
       body(cur, smem + ((p.nbuf == 2) ? (cc & 1) : 0) * bufbytes, sbc, r, sb);
       if (chunk_end) {
         if (!last_chunk) {
           if (p.nbuf == 2) {
-            h_commit(hs, p, Bp, next_c, smem + ((cc + 1) & 1) * bufbytes);
+            h_commit(hs, p, next_c, smem + ((cc + 1) & 1) * bufbytes);
             __syncthreads();
           } else {
             __syncthreads();
-            h_commit(hs, p, Bp, next_c, smem);
+            h_commit(hs, p, next_c, smem);
             __syncthreads();
           }
         }
@@ -449,12 +479,12 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
 }
 
 template <bool FAST, bool RESIDENT, int RING, class Body, class RoundEnd>
-__device__ __forceinline__ void stream_driver(const StreamParams& p, const TileRange& tr, int Bp, unsigned char* smem,
+__device__ __forceinline__ void stream_driver(const StreamParams& p, const TileRange& tr, unsigned char* smem,
                                               Body&& body, RoundEnd&& round_end) {
   if (FAST)
-    stream_driver_fast<RING, RESIDENT>(p, tr, Bp, smem, body, round_end);
+    stream_driver_fast<RING, RESIDENT>(p, tr, smem, body, round_end);
   else
-    stream_driver_general<RESIDENT>(p, tr, Bp, smem, body, round_end);
+    stream_driver_general<RESIDENT>(p, tr, smem, body, round_end);
 }
 
 // ---------------------------------------------------------------------------
@@ -466,7 +496,13 @@ __device__ __forceinline__ void stream_driver(const StreamParams& p, const TileR
 // round is finished after the stream.  The ALU work of the epilogue is thereby
 // spread over bodies whose W loads are already in flight.
 // ---------------------------------------------------------------------------
-template <int NB, int EPI, bool RESIDENT, bool FAST, int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
+// NOISE_LDS: the epilogue reads the tile's noise table staged in LDS before
+// the stream (noise_stage); otherwise it runs Philox itself.  The two are
+// separate kernels on purpose: with the Philox code inside the streaming loop
+// the W stream ran about 9% slower on gfx950 even on rounds that took the
+// table path, so the table kernels carry no Philox code in the loop at all.
+template <int NB, int EPI, bool RESIDENT, bool FAST, bool MASKED, bool NOISE_LDS,
+          int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int Bp = NB * 16;
@@ -476,7 +512,16 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   const int rs = p.h_rowstride;
   uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
   const int64_t mw_lo = mask_w_lo(p, tr);
-  mask_stage(p, tr, mask_lds);  // made visible by the driver's first barrier
+  if (MASKED) mask_stage(p, tr, mask_lds);  // made visible by the driver's first barrier
+  const float* noise_lds = (const float*)(smem + p.noise_lds_off);
+  if (EPI != EPI_STORE && NOISE_LDS) noise_stage(p, tr, (float*)noise_lds);  // ditto
+  // H row of this lane in each 16-wide batch block (padding lanes read the zero row)
+  int hoff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = nb * 16 + l16;
+    hoff[nb] = grp * 128 + (row < p.B ? row : p.h_rows - 1) * rs;
+  }
 
   float bv[NB], lm[NB], ls[NB];
   int32_t bi[NB];
@@ -498,14 +543,14 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   // while the MFMAs of step j run.  (Left to itself the compiler waits on each
   // LDS read right before its MFMA, and the loop becomes bound by LDS latency.)
   auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc) {
-    const unsigned char* hb = hbase + sbc * 512 + grp * 128 + l16 * rs;
+    const unsigned char* hb = hbase + sbc * 512;
     u32x4_t h0[NB], h1[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + nb * 16 * rs);
+    for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb]);
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + nb * 16 * rs + (j + 1) * 16);
+      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 1) * 16);
       __builtin_amdgcn_sched_barrier(0);  // reads of step j + 1 stay ahead of the MFMAs of step j
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -513,7 +558,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
                                                           __builtin_bit_cast(bf16x8_t, h0[nb]), acc[nb], 0, 0, 0);
       if (j + 2 < 8) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + nb * 16 * rs + (j + 2) * 16);
+        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 2) * 16);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -540,8 +585,13 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
           if (v0 + i < p.V) dst[i] = a4[i];
       }
     } else {
-      const uint32_t bits = mask_bits4(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
-      epilogue_quad<EPI>(p, v0, b, a4, bits, bv[nb], bi[nb], lm[nb], ls[nb]);
+      const uint32_t bits = mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
+      f32x4_t g;
+      if (NOISE_LDS)
+        g = *(const f32x4_t*)(noise_lds + b * p.noise_pitch + (int)(v0 - tr.mb_lo * 16));
+      else
+        g = noise_quad(p, (int)(p.vocab_offset + v0), (uint32_t)(p.row_offset + b));
+      epilogue_quad<EPI>(p, (int)v0, a4, g, bits, bv[nb], bi[nb], lm[nb], ls[nb]);
     }
   };
 
@@ -573,7 +623,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING>(p, tr, Bp, smem, body, round_end);
+  stream_driver<FAST, RESIDENT, RING>(p, tr, smem, body, round_end);
   if (kDefer && tr.rounds > 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) finish_nb(tr.rounds - 1, nb);
@@ -634,7 +684,8 @@ __device__ __forceinline__ float dot8(const u32x4_t w, const u32x4_t h, float c)
   return c;
 }
 
-template <int BD, int EPI, bool RESIDENT, bool FAST, int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
+template <int BD, int EPI, bool RESIDENT, bool FAST, bool MASKED,
+          int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p) {
   static_assert(BD <= 2, "dot kernel handles at most 2 batch rows");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -644,7 +695,7 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
   const int rs = p.h_rowstride;
   uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
   const int64_t mw_lo = mask_w_lo(p, tr);
-  mask_stage(p, tr, mask_lds);
+  if (MASKED) mask_stage(p, tr, mask_lds);
 
   float bv = -INFINITY, lm = -INFINITY, ls = 0.0f;
   int32_t bi = -1;
@@ -698,7 +749,7 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
     const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)(gv >> 2), (uint32_t)grow, p.step_lo, p.step_hi);
     const uint32_t q = (uint32_t)(gv & 3);
     const uint32_t word = q == 0 ? r.w[0] : q == 1 ? r.w[1] : q == 2 ? r.w[2] : r.w[3];
-    const bool ok = v < p.V && ((mask_bits4(p, mask_lds, mw_lo, gv & ~(int64_t)3, b) >> q) & 1u);
+    const bool ok = v < p.V && ((mask_bits4<MASKED>(p, mask_lds, mw_lo, gv & ~(int64_t)3, b) >> q) & 1u);
     const float sc = xv * p.inv_t;
     const float pv = ok ? sc + gumbel_from_bits(word) : -INFINITY;
     if (pv > bv) {
@@ -720,7 +771,7 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING>(p, tr, BD, smem, body, round_end);
+  stream_driver<FAST, RESIDENT, RING>(p, tr, smem, body, round_end);
   if (tr.rounds > 0) finish_round(tr.rounds - 1);
   if (EPI == EPI_STORE) return;
 
@@ -773,29 +824,42 @@ static hipError_t launch_with_lds(K kernel, int grid, int lds, hipStream_t strea
   return hipGetLastError();
 }
 
-template <int EPI, bool RES, bool FAST>
+template <int EPI, bool RES, bool FAST, bool MK, bool NZ>
 static hipError_t launch_variant(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
   const int g = p.n_tiles, L = c.lds_bytes;
   if (c.dot) {
     switch (c.bd) {
-      case 1: return launch_with_lds(fmms_dot_kernel<1, EPI, RES, FAST>, g, L, s, p);
-      case 2: return launch_with_lds(fmms_dot_kernel<2, EPI, RES, FAST>, g, L, s, p);
+      case 1: return launch_with_lds(fmms_dot_kernel<1, EPI, RES, FAST, MK>, g, L, s, p);
+      case 2: return launch_with_lds(fmms_dot_kernel<2, EPI, RES, FAST, MK>, g, L, s, p);
       default: return hipErrorInvalidValue;
     }
   }
   switch (c.nb) {
-    case 1: return launch_with_lds(fmms_mfma_kernel<1, EPI, RES, FAST>, g, L, s, p);
-    case 2: return launch_with_lds(fmms_mfma_kernel<2, EPI, RES, FAST>, g, L, s, p);
-    case 4: return launch_with_lds(fmms_mfma_kernel<4, EPI, RES, FAST>, g, L, s, p);
+    case 1: return launch_with_lds(fmms_mfma_kernel<1, EPI, RES, FAST, MK, NZ>, g, L, s, p);
+    case 2: return launch_with_lds(fmms_mfma_kernel<2, EPI, RES, FAST, MK, NZ>, g, L, s, p);
+    case 4: return launch_with_lds(fmms_mfma_kernel<4, EPI, RES, FAST, MK, NZ>, g, L, s, p);
     default: return hipErrorInvalidValue;
   }
 }
 
+// The noise table is planned only for the fast driver and the sampling epilogues.
+template <int EPI, bool MK>
+static hipError_t launch_masking(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
+  const bool res = p.nchunk == 1;
+  if (c.fast) {
+    if (EPI != EPI_STORE && p.noise_pitch > 0 && !c.dot)
+      return res ? launch_variant<EPI, true, true, MK, EPI != EPI_STORE>(p, c, s)
+                 : launch_variant<EPI, false, true, MK, EPI != EPI_STORE>(p, c, s);
+    return res ? launch_variant<EPI, true, true, MK, false>(p, c, s) : launch_variant<EPI, false, true, MK, false>(p, c, s);
+  }
+  return res ? launch_variant<EPI, true, false, MK, false>(p, c, s) : launch_variant<EPI, false, false, MK, false>(p, c, s);
+}
+
+// The stored-logits epilogue never reads the mask.
 template <int EPI>
 hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
-  const bool res = p.nchunk == 1;
-  if (res) return c.fast ? launch_variant<EPI, true, true>(p, c, s) : launch_variant<EPI, true, false>(p, c, s);
-  return c.fast ? launch_variant<EPI, false, true>(p, c, s) : launch_variant<EPI, false, false>(p, c, s);
+  if (EPI != EPI_STORE && p.mask) return launch_masking<EPI, EPI != EPI_STORE>(p, c, s);
+  return launch_masking<EPI, false>(p, c, s);
 }
 
 }  // namespace fsk
