@@ -94,6 +94,7 @@ int choose_config(int B, int path, fsk::StreamConfig& cfg) {
   cfg.bd = dot ? pow2_at_least(B) : 0;
   cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : 4);
   cfg.fast = false;
+  cfg.rm = 0;
   cfg.lds_bytes = 0;
   return FS_OK;
 }

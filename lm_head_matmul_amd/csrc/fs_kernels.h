@@ -76,6 +76,7 @@ struct StreamConfig {
   int nb;       // MFMA: 16-wide batch blocks (1, 2, 4)
   int bd;       // dot: padded batch (1, 2)
   bool fast;    // straight-line fast driver (see fs_stream.h)
+  int rm;       // chunked H with the fast driver: rounds per chunk-outer pass (0: round-major kernel)
   int lds_bytes;
 };
 
@@ -87,6 +88,7 @@ constexpr int kDotMaxB = 2;
 constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
 constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
+constexpr int kKouterMaxRounds = 5;  // accumulator sets a wave keeps in registers in the chunk-outer kernel
 constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
 
 // Mask words per row staged for the largest tile of a launch.

@@ -234,7 +234,14 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     cfg.fast = full_k && p.nsub % kFastRingResident == 0;
   else
     cfg.fast = full_k && p.cs == kFastRingChunked && p.nbuf == 2 && p.nsub % kFastRingChunked == 0;
-  if (!cfg.dot && cfg.fast && epi != EPI_STORE) {
+  // Chunked H with the fast driver: the chunk-outer kernel, whose passes cover
+  // up to kKouterMaxRounds rounds (one pass for most tiles).
+  cfg.rm = 0;
+  if (!cfg.dot && cfg.fast && p.nchunk > 1) {
+    const int64_t rounds = (tile_rows / 16 + kWaves - 1) / kWaves;
+    cfg.rm = (int)(rounds < kKouterMaxRounds ? rounds : kKouterMaxRounds);
+  }
+  if (!cfg.dot && cfg.fast && cfg.rm == 0 && epi != EPI_STORE) {
     const int pitch = (int)tile_rows + 4;
     const int64_t nbytes = (int64_t)p.B * pitch * 4;
     if (total + nbytes <= kLdsMax) {

@@ -191,6 +191,19 @@ __device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], c
   }
 }
 
+// Stage H chunk `cidx` (two 256-wide sub-blocks: 1 KB per row) straight from
+// global memory into LDS, without registers: one wave instruction moves one row
+// (lane l carries bytes [16 l, 16 l + 16) of it).  Rows b < B only (wave
+// b % kWaves issues row b); the zero row is written once at kernel start.  The
+// loads retire in order with the W loads of the issuing wave.
+__device__ __forceinline__ void h_chunk_dma(const StreamParams& p, int cidx, unsigned char* buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* src = p.H + cidx * 512 + lane * 8;
+  for (int b = wave; b < p.B; b += kWaves)
+    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)b * p.ldh),
+                                     (__attribute__((address_space(3))) void*)(buf + b * p.h_rowstride), 16, 0, 0);
+}
+
 // The vocabulary mask of the tile, staged in LDS at kernel start: rows b < B,
 // words [w_lo, w_lo + p.mask_words) of each row (the host sizes batch chunks so
 // that it always fits).  Reading mask bits from LDS keeps global loads out of
@@ -339,12 +352,19 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
     }
   };
 
-  u32x4_t hs[kMaxStagePieces];
+  // Chunked H (chunks of U = 2 sub-blocks, 1 KB per row): chunks are copied
+  // straight into LDS (h_chunk_dma), the zero row of both buffers once here.
+  static_assert(RESIDENT || U == 2, "chunked H in the fast driver: two sub-blocks per chunk");
   if (RESIDENT) {
     h_stage_all(p, 0, smem);
   } else {
-    h_prefetch(hs, p, 0);
-    h_commit(hs, p, 0, smem);
+    for (int i = threadIdx.x; i < (p.h_rows - p.B) * 64; i += kThreads) {
+      const int row = p.B + i / 64, q = i % 64;
+      *(u32x4_t*)(smem + row * p.h_rowstride + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
+      *(u32x4_t*)(smem + bufbytes + row * p.h_rowstride + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    h_chunk_dma(p, 0, smem);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS copies have landed
   }
   __syncthreads();
 
@@ -361,9 +381,10 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
       for (int k = 0; k < U; ++k) {
         load(buf[(k + U - 1) % U], lr, lsb);
         advance();
-        // the chunk after this one (chunk index == group index); past the last
-        // group of the last round this stages an unused copy of chunk 0
-        if (!RESIDENT && k == 0) h_prefetch(hs, p, g + 1 < ngrp ? g + 1 : 0);
+        // the chunk after this one (chunk index == group index) into the other
+        // buffer; past the last group of the last round this copies chunk 0
+        // once more, unused
+        if (!RESIDENT && k == 0) h_chunk_dma(p, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
         // keep the loads above ahead of the compute below: the scheduler would
         // otherwise sink them under the MFMAs to save registers
         __builtin_amdgcn_sched_barrier(0);
@@ -372,7 +393,9 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
         else
           body(buf[k], smem + (cc & 1) * bufbytes, k, r, g * U + k);
         if (!RESIDENT && k == U - 1) {
-          h_commit(hs, p, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
+          // the copies were issued before the last W sub-block's 8 loads: once
+          // at most those remain outstanding (vmcnt 8), this wave's copies landed
+          __builtin_amdgcn_s_waitcnt(0xF78);
           __syncthreads();
           ++cc;
         }
@@ -485,6 +508,48 @@ __device__ __forceinline__ void stream_driver(const StreamParams& p, const TileR
     stream_driver_fast<RING, RESIDENT>(p, tr, smem, body, round_end);
   else
     stream_driver_general<RESIDENT>(p, tr, smem, body, round_end);
+}
+
+// End of an MFMA streaming kernel: reduce each wave's maximizers over its four
+// lane groups (lanes l16, l16 + 16, l16 + 32, l16 + 48 share a batch column),
+// then over the waves through LDS, and publish the tile's entry.
+template <int EPI, int NB>
+__device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned char* smem, float (&bv)[NB],
+                                                 int32_t (&bi)[NB], float (&lm)[NB], float (&ls)[NB]) {
+  constexpr int Bp = NB * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float ov = __shfl_xor(bv[nb], off);
+      const int32_t oi = __shfl_xor(bi[nb], off);
+      merge_best(bv[nb], bi[nb], ov, oi);
+      if (EPI == EPI_GROUP) {
+        const float om = __shfl_xor(lm[nb], off);
+        const float os = __shfl_xor(ls[nb], off);
+        lse_merge(lm[nb], ls[nb], om, os);
+      }
+    }
+  }
+  __syncthreads();  // H buffers are free: reuse LDS as scratch
+  float* sv = (float*)smem;
+  int32_t* si = (int32_t*)(sv + kWaves * Bp);
+  float* sm = (float*)(si + kWaves * Bp);
+  float* ss = sm + kWaves * Bp;
+  if (grp == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = nb * 16 + l16;
+      sv[wave * Bp + b] = bv[nb];
+      si[wave * Bp + b] = bi[nb];
+      sm[wave * Bp + b] = lm[nb];
+      ss[wave * Bp + b] = ls[nb];
+    }
+  }
+  __syncthreads();
+  publish_tile<EPI>(p, Bp, sv, si, sm, ss);
 }
 
 // ---------------------------------------------------------------------------
@@ -630,38 +695,193 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   }
   if (EPI == EPI_STORE) return;
 
-  // Reduce inside the wave: lanes l16, l16 + 16, l16 + 32, l16 + 48 share a column.
+  finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
+}
+
+
+// ---------------------------------------------------------------------------
+// Chunk-outer MFMA kernel, for H that does not fit in LDS (fast shapes: chunks
+// of exactly kFastRingChunked 256-wide sub-blocks).  The round-major kernel
+// restages every H chunk once per round; here each pass over the tile covers
+// RM rounds and loops chunk-outer: for each chunk c, for each round r < RM,
+// for each sub-block s of the chunk, W[block of round r][k range (c, s)] is
+// streamed and accumulated into acc[r] (RM * NB accumulator sets stay in
+// registers).  Each chunk is thereby staged once per pass instead of once per
+// round.  Rounds past the wave's last block re-read that block (recently
+// fetched, so an L2 hit) and their results are dropped.  The rounds of a pass
+// are finished (scale, mask, noise, argmax) after its last chunk.
+// ---------------------------------------------------------------------------
+template <int NB, int EPI, bool MASKED, int RM>
+__global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParams p) {
+  static_assert(kFastRingChunked == 2, "two sub-blocks per chunk, two register buffers");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const TileRange tr = tile_range(p);
+  const int rs = p.h_rowstride;
+  const int bufbytes = p.h_rows * rs;
+  uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
+  const int64_t mw_lo = mask_w_lo(p, tr);
+  if (MASKED) mask_stage(p, tr, mask_lds);  // made visible by the first barrier below
+  int hoff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float ov = __shfl_xor(bv[nb], off);
-      const int32_t oi = __shfl_xor(bi[nb], off);
-      merge_best(bv[nb], bi[nb], ov, oi);
-      if (EPI == EPI_GROUP) {
-        const float om = __shfl_xor(lm[nb], off);
-        const float os = __shfl_xor(ls[nb], off);
-        lse_merge(lm[nb], ls[nb], om, os);
-      }
-    }
+    const int row = nb * 16 + l16;
+    hoff[nb] = grp * 128 + (row < p.B ? row : p.h_rows - 1) * rs;
   }
-  __syncthreads();  // H buffers are free: reuse LDS as scratch
-  float* sv = (float*)smem;
-  int32_t* si = (int32_t*)(sv + kWaves * Bp);
-  float* sm = (float*)(si + kWaves * Bp);
-  float* ss = sm + kWaves * Bp;
-  if (grp == 0) {
+  float bv[NB], lm[NB], ls[NB];
+  int32_t bi[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    bv[nb] = -INFINITY;
+    bi[nb] = -1;
+    lm[nb] = -INFINITY;
+    ls[nb] = 0.0f;
+  }
+  f32x4_t acc[RM][NB];
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = p.nchunk;
+  const int npass = (tr.rounds + RM - 1) / RM;
+  // the wave's last block of the tile (the clamp target of empty rounds)
+  const int64_t nown = tr.mb_hi - tr.mb_lo - wave > 0 ? (tr.mb_hi - tr.mb_lo - wave + kWaves - 1) / kWaves : 0;
+  const int64_t last_blk = nown > 0 ? tr.mb_lo + (nown - 1) * kWaves + wave : tr.mb_hi - 1;
+  auto row_ptr = [&](int pass, int r) {
+    int64_t mb = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
+    mb = mb < tr.mb_hi ? mb : last_blk;
+    return w_row(p, tr, mb, l16) + grp * 64;
+  };
+  auto load = [&](u32x4_t (&buf)[8], const uint16_t* row, int sb) {
+    const u32x4_t* src = (const u32x4_t*)(row + sb * 256);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) buf[e] = src[e];
+  };
+  auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hb, f32x4_t (&a)[NB]) {
+    u32x4_t h0[NB], h1[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb]);
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 1) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        a[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
+                                                        __builtin_bit_cast(bf16x8_t, h0[nb]), a[nb], 0, 0, 0);
+      if (j + 2 < 8) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 2) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        a[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j + 1]),
+                                                        __builtin_bit_cast(bf16x8_t, h1[nb]), a[nb], 0, 0, 0);
+    }
+  };
+  auto finish = [&](int pass, int r, const f32x4_t (&a)[NB]) {
+    const int64_t mbg = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
+    if (mbg >= tr.mb_hi) return;
+    const int64_t v0 = mbg * 16 + grp * 4;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int b = nb * 16 + l16;
-      sv[wave * Bp + b] = bv[nb];
-      si[wave * Bp + b] = bi[nb];
-      sm[wave * Bp + b] = lm[nb];
-      ss[wave * Bp + b] = ls[nb];
+      if (b >= p.B) continue;
+      if (EPI == EPI_STORE) {
+        float* dst = p.logits + (int64_t)b * p.ldl + v0;
+        if (v0 + 3 < p.V) {
+          *(f32x4_t*)dst = a[nb];
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (v0 + i < p.V) dst[i] = a[nb][i];
+        }
+      } else {
+        const float a4[4] = {a[nb][0], a[nb][1], a[nb][2], a[nb][3]};
+        const uint32_t bits = mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
+        const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), (uint32_t)(p.row_offset + b));
+        epilogue_quad<EPI>(p, (int)v0, a4, g, bits, bv[nb], bi[nb], lm[nb], ls[nb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one N-block's noise at a time (register pressure)
+    }
+  };
+
+  if (tr.rounds > 0) {
+    // zero rows (the padding lanes' row) of both buffers, then chunk 0
+    for (int i = tid; i < (p.h_rows - p.B) * 64; i += kThreads) {
+      const int row = p.B + i / 64, q = i % 64;
+      *(u32x4_t*)(smem + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
+      *(u32x4_t*)(smem + bufbytes + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    h_chunk_dma(p, 0, smem);
+    __builtin_amdgcn_s_waitcnt(0);  // the LDS copies of this wave have landed
+    __syncthreads();
+
+    const uint16_t* rowp[RM];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) rowp[r] = row_ptr(0, r);
+    u32x4_t buf[2][8];
+    load(buf[0], rowp[0], 0);
+    int cc = 0;  // chunks consumed
+    for (int pass = 0; pass < npass; ++pass) {
+      // Waves own RM or RM - 1 blocks in a pass (tiles differ by at most one
+      // block); a wave without a block in the pass's last round skips that
+      // round instead of re-reading data: its round RM - 2 goes straight on to
+      // the next chunk.  Both paths leave the same 8 loads in flight into the
+      // same registers, so the wait counts agree where they join.
+      const bool last_on = nown >= (int64_t)(pass + 1) * RM;
+      for (int c = 0; c < nchunk; ++c) {
+        const unsigned char* hb = smem + (cc & 1) * bufbytes;
+        const int nc = c + 1 < nchunk ? c + 1 : 0;  // the chunk staged next
+        const bool last_c = c + 1 == nchunk;
+        const int np = last_c && pass + 1 < npass ? pass + 1 : pass;
+        const uint16_t* next_row = last_c ? row_ptr(np, 0) : rowp[0];  // first item of the next chunk
+        const int next_sb = last_c ? 0 : (c + 1) * 2;
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+          if (r == RM - 1 && RM > 1 && !last_on) break;
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            // the W item after (r, sb): same round's next sub-block, the next
+            // round's first one, or the first one of the next chunk / pass
+            if (sb == 0) {
+              load(buf[1], rowp[r], c * 2 + 1);
+            } else if (r + 2 < RM || (r + 2 == RM && RM > 1)) {
+              if (r + 2 == RM)  // the next round is the last one: it may be skipped
+                load(buf[0], last_on ? rowp[r + 1] : next_row, last_on ? c * 2 : next_sb);
+              else
+                load(buf[0], rowp[r + 1], c * 2);
+            } else {
+              load(buf[0], next_row, next_sb);
+            }
+            if (r == 0 && sb == 0) h_chunk_dma(p, nc, smem + ((cc + 1) & 1) * bufbytes);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(buf[sb], hb + sb * 512, acc[r]);
+          }
+        }
+        // the chunk's copies were issued before the last W item (8 loads), so
+        // at most those 8 loads may still be outstanding: vmcnt(8)
+        __builtin_amdgcn_s_waitcnt(0xF78);
+        __syncthreads();
+        ++cc;
+      }
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        finish(pass, r, acc[r]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if (pass + 1 < npass) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) rowp[r] = row_ptr(pass + 1, r);
+      }
     }
   }
-  __syncthreads();
-  publish_tile<EPI>(p, Bp, sv, si, sm, ss);
+  if (EPI == EPI_STORE) return;
+  finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
 }
 
 // ---------------------------------------------------------------------------
@@ -842,10 +1062,31 @@ static hipError_t launch_variant(const StreamParams& p, const StreamConfig& c, h
   }
 }
 
+template <int EPI, bool MK, int NB>
+static hipError_t launch_kouter(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
+  const int g = p.n_tiles, L = c.lds_bytes;
+  switch (c.rm) {
+    case 1: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 1>, g, L, s, p);
+    case 2: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 2>, g, L, s, p);
+    case 3: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 3>, g, L, s, p);
+    case 4: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 4>, g, L, s, p);
+    case 5: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 5>, g, L, s, p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // The noise table is planned only for the fast driver and the sampling epilogues.
 template <int EPI, bool MK>
 static hipError_t launch_masking(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
   const bool res = p.nchunk == 1;
+  if (c.rm > 0 && !c.dot) {
+    switch (c.nb) {
+      case 1: return launch_kouter<EPI, MK, 1>(p, c, s);
+      case 2: return launch_kouter<EPI, MK, 2>(p, c, s);
+      case 4: return launch_kouter<EPI, MK, 4>(p, c, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (c.fast) {
     if (EPI != EPI_STORE && p.noise_pitch > 0 && !c.dot)
       return res ? launch_variant<EPI, true, true, MK, EPI != EPI_STORE>(p, c, s)
