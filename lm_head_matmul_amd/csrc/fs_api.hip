@@ -26,6 +26,10 @@ struct fs_ctx {
   float* ws_m;
   float* ws_s;
   void* base;
+  // top-k: fp32 scores of up to topk_rows batch rows, [topk_rows][topk_ldl]
+  float* topk_ws;
+  int64_t topk_ldl;
+  int topk_rows;
 };
 
 namespace {
@@ -183,6 +187,31 @@ int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t str
   return FS_OK;
 }
 
+// Top-k sampling of batch rows [r0, r0 + rows) whose unscaled logits are in
+// logits (row r0 first).
+int launch_topk(const float* logits, int64_t ldl, int rows, int r0, int64_t V, float temperature, uint64_t seed,
+                uint64_t step, const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, hipStream_t s) {
+  fsk::TopkParams q;
+  std::memset(&q, 0, sizeof q);
+  q.logits = logits;
+  q.ldl = ldl;
+  q.B = rows;
+  q.V = (int)V;
+  q.inv_t = 1.0f / temperature;
+  q.seed_lo = (uint32_t)seed;
+  q.seed_hi = (uint32_t)(seed >> 32);
+  q.step_lo = (uint32_t)step;
+  q.step_hi = (uint32_t)(step >> 32);
+  q.mask = mask;
+  q.ldm = ldm;
+  q.row_offset = r0;
+  q.top_k = top_k;
+  q.out_idx = out_idx + r0;
+  hipError_t e = fsk::launch_topk_sample(q, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k sampling kernel launch");
+  return FS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,6 +261,16 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     delete c;
     return hip_fail(e, "hipMemset(workspace)");
   }
+  if (max_top_k > 0) {
+    c->topk_rows = max_B < fsk::kMfmaMaxB ? max_B : fsk::kMfmaMaxB;
+    c->topk_ldl = (max_V + 3) / 4 * 4;
+    e = hipMalloc(&c->topk_ws, (size_t)c->topk_rows * (size_t)c->topk_ldl * sizeof(float));
+    if (e != hipSuccess) {
+      (void)hipFree(c->base);
+      delete c;
+      return hip_fail(e, "hipMalloc(top-k workspace)");
+    }
+  }
   *out = c;
   return FS_OK;
 }
@@ -240,6 +279,7 @@ void fs_destroy(fs_ctx* ctx) {
   if (!ctx) return;
   DeviceGuard guard(ctx->device);
   if (ctx->base) (void)hipFree(ctx->base);
+  if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
   delete ctx;
 }
 
@@ -268,12 +308,30 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
   if (!out_idx) return fail(FS_ERR_INVALID_ARG, "out_idx is NULL");
   if (top_k < 0 || top_k > ctx->max_top_k)
     return fail(top_k < 0 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY, "top_k=%d outside [0, max_top_k=%d]", top_k, ctx->max_top_k);
-  if (top_k > 0) return fail(FS_ERR_UNSUPPORTED, "top_k > 0 is not implemented by this build");
   if ((tile_max == nullptr) != (tile_arg == nullptr)) return fail(FS_ERR_INVALID_ARG, "tile_max and tile_arg go together");
+  if (top_k > 0 && tile_max) return fail(FS_ERR_INVALID_ARG, "tile maxima are reported with top_k == 0 only");
   if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
   DeviceGuard guard(ctx->device);
   if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
   fsk::StreamParams p;
+  if (top_k > 0) {
+    // The exact top-k boundary of a row needs all of its scores: the streaming
+    // pass stores them into the context's workspace (batch chunks of
+    // topk_rows rows) and a per-row selection kernel samples the kept set.
+    hipStream_t s = (hipStream_t)stream;
+    for (int r0 = 0; r0 < B; r0 += ctx->topk_rows) {
+      const int Bc = (B - r0) < ctx->topk_rows ? (B - r0) : ctx->topk_rows;
+      fill_common(p, ctx, H + (int64_t)r0 * ldh, ldh, W, ldw, Bc, d, V, temperature, seed, step, nullptr, 0);
+      rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int q0) {
+        c.logits = ctx->topk_ws + (int64_t)q0 * ctx->topk_ldl;
+        c.ldl = ctx->topk_ldl;
+      });
+      if (rc != FS_OK) return rc;
+      rc = launch_topk(ctx->topk_ws, ctx->topk_ldl, Bc, r0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
+      if (rc != FS_OK) return rc;
+    }
+    return FS_OK;
+  }
   fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
   const int nt = p.n_tiles;
   return run_stream_chunks(p, path, fsk::EPI_FLAT, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
@@ -294,7 +352,6 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   if (ldl < V || ldl % 4 != 0) return fail(FS_ERR_INVALID_ARG, "ldl=%lld must be >= V and a multiple of 4", (long long)ldl);
   if (top_k < 0 || top_k > ctx->max_top_k)
     return fail(top_k < 0 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY, "top_k=%d outside [0, max_top_k=%d]", top_k, ctx->max_top_k);
-  if (top_k > 0) return fail(FS_ERR_UNSUPPORTED, "top_k > 0 is not implemented by this build");
   if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
   DeviceGuard guard(ctx->device);
   if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
@@ -306,6 +363,7 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
     c.ldl = ldl;
   });
   if (rc != FS_OK) return rc;
+  if (top_k > 0) return launch_topk(logits_ws, ldl, B, 0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
   fsk::SampleParams q;
   std::memset(&q, 0, sizeof q);
   q.logits = logits_ws;

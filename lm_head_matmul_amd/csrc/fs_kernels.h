@@ -70,6 +70,21 @@ struct SampleParams {  // unfused second pass: sample from stored logits
   int32_t* out_idx;
 };
 
+// Top-k sampling from stored fp32 logits, one workgroup per batch row.
+struct TopkParams {
+  const float* logits;  // [B][ldl], row b holds global batch row row_offset + b
+  int64_t ldl;
+  int B;
+  int V;
+  float inv_t;
+  uint32_t seed_lo, seed_hi, step_lo, step_hi;
+  const uint32_t* mask;  // [*, ldm] words indexed by the global batch row, or null
+  int64_t ldm;
+  int row_offset;
+  int top_k;
+  int32_t* out_idx;  // [B]
+};
+
 // Kernel selection for a streaming launch.
 struct StreamConfig {
   bool dot;     // dot-product kernel (else MFMA)
@@ -104,6 +119,7 @@ hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi
 template <int EPI>
 hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& cfg, hipStream_t stream);
 hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream);
+hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream);
 hipError_t launch_group_combine(const GroupSummary* s, int n_groups, int B, uint64_t seed, uint64_t step, int mode,
                                 int32_t* out_idx, hipStream_t stream);
 hipError_t launch_debug_philox(uint64_t seed, uint64_t step, uint32_t row, int64_t v0, int64_t n, uint32_t* r_out,

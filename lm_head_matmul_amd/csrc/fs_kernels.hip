@@ -64,6 +64,213 @@ __global__ void __launch_bounds__(kThreads) sample_logits_kernel(const SamplePar
 }
 
 // ---------------------------------------------------------------------------
+// Top-k sampling from stored logits.  Per row (one workgroup): exact top-k of
+// the allowed scores s = logit * (1/T) by a most-significant-digit radix
+// select on order-preserving 32-bit keys, ties at the boundary kept by lower
+// id; then the Gumbel-max over the kept ids.  [readus.org FlashSampling
+// summary, section on Top-K and masking: the sampler acts on the kept set]
+//
+//   level 0 histogram of key bits 31..20 over the row; the bin where the count
+//   from the top reaches k is the boundary; keys in higher bins are kept.
+//   If the boundary bin holds at most kTopkCap keys they are gathered into
+//   LDS and sorted by (key desc, id asc); else the bin is refined on bits
+//   19..8 and 7..0.  A boundary of more than kTopkCap equal keys is resolved
+//   by a pass in id order.
+// ---------------------------------------------------------------------------
+constexpr int kTopkCap = 4096;
+
+// Order-preserving key of a score, with -0 folded onto +0 (they compare equal).
+__device__ __forceinline__ uint32_t score_key(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ void __launch_bounds__(kThreads) topk_sample_kernel(const TopkParams p) {
+  __shared__ uint32_t hist[4096];
+  __shared__ uint64_t cand[kTopkCap];
+  __shared__ int s_bin, s_above, s_inbin, s_total, s_ncand, s_run;
+  __shared__ float red_v[kWaves];
+  __shared__ int32_t red_i[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const float* L = p.logits + (int64_t)b * p.ldl;
+  const uint32_t grow = (uint32_t)(p.row_offset + b);
+  const uint32_t* M = p.mask ? p.mask + (int64_t)grow * p.ldm : nullptr;
+  const int V = p.V;
+  auto allowed = [&](int v) { return M == nullptr || ((M[v >> 5] >> (v & 31)) & 1u); };
+  auto score = [&](int v) { return L[v] * p.inv_t; };
+
+  float bv = -INFINITY;
+  int32_t bi = -1;
+  auto take = [&](int v, float s) {  // kept id: perturb and update the maximizer
+    const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)v >> 2, grow, p.step_lo, p.step_hi);
+    const uint32_t q = (uint32_t)v & 3u;
+    const uint32_t w = q == 0 ? r.w[0] : q == 1 ? r.w[1] : q == 2 ? r.w[2] : r.w[3];
+    merge_best(bv, bi, s + gumbel_from_bits(w), v);
+  };
+
+  // --- radix select of the boundary ---------------------------------------
+  uint32_t prefix = 0, pmask = 0;
+  int need = p.top_k;
+  bool keep_all = false;
+  int shift = 20, nbins = 4096;
+  int level = 0;
+  for (; level < 3; ++level) {
+    for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    for (int v = tid; v < V; v += kThreads) {
+      if (!allowed(v)) continue;
+      const uint32_t k = score_key(score(v));
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins [hi - (l + 1) * per, hi - l * per) counted from the top
+      const int per = nbins / 64;
+      const int top = nbins - 1 - lane * per;
+      int local = 0;
+      for (int j = 0; j < per; ++j) local += (int)hist[top - j];
+      int incl = local;  // inclusive prefix over lanes 0..lane (from the top)
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const int excl = incl - local;
+      const int total = __shfl(incl, 63);
+      if (lane == 0) s_total = total;
+      if (excl < need && incl >= need) {  // the boundary lies in this lane's bins
+        int run = excl;
+        for (int j = 0; j < per; ++j) {
+          const int c = (int)hist[top - j];
+          if (run + c >= need) {
+            s_bin = top - j;
+            s_above = run;
+            s_inbin = c;
+            break;
+          }
+          run += c;
+        }
+      }
+    }
+    __syncthreads();
+    if (level == 0 && s_total <= need) {  // no more allowed ids than k: keep them all
+      keep_all = true;
+      break;
+    }
+    need -= s_above;
+    prefix |= (uint32_t)s_bin << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    if (s_inbin <= kTopkCap) break;
+    if (level == 0) {
+      shift = 8;
+      nbins = 4096;
+    } else {
+      shift = 0;
+      nbins = 256;
+    }
+    __syncthreads();  // s_* are rewritten by the next level
+  }
+  const bool gather = keep_all || level < 3;
+
+  // --- kept ids above the boundary; boundary candidates into LDS ------------
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+  if (gather) {
+    for (int v = tid; v < V; v += kThreads) {
+      if (!allowed(v)) continue;
+      const float s = score(v);
+      const uint32_t k = score_key(s);
+      const uint32_t hi = k & pmask;
+      if (keep_all || hi > prefix) {
+        take(v, s);
+      } else if (hi == prefix) {
+        const int at = atomicAdd(&s_ncand, 1);
+        cand[at] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+      }
+    }
+    __syncthreads();
+    if (!keep_all) {
+      // bitonic sort, descending, of the candidates (padded with zeros)
+      const int n = s_ncand;
+      int np2 = 1;
+      while (np2 < n) np2 <<= 1;
+      for (int i = n + tid; i < np2; i += kThreads) cand[i] = 0;
+      __syncthreads();
+      for (int kk = 2; kk <= np2; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+          for (int i = tid; i < np2; i += kThreads) {
+            const int ij = i ^ j;
+            if (ij > i) {
+              const uint64_t x = cand[i], y = cand[ij];
+              const bool desc = (i & kk) == 0;
+              if (desc ? (x < y) : (x > y)) {
+                cand[i] = y;
+                cand[ij] = x;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      }
+      for (int i = tid; i < need && i < n; i += kThreads) {
+        const int v = (int)(0xFFFFFFFFu - (uint32_t)(cand[i] & 0xFFFFFFFFu));
+        take(v, score(v));
+      }
+    }
+  } else {
+    // more than kTopkCap ids share the exact boundary key: keys above it are
+    // kept, and of those equal to it the `need` lowest ids, found in id order
+    if (tid == 0) s_run = 0;
+    __syncthreads();
+    for (int base = 0; base < V; base += kThreads) {
+      const int v = base + tid;
+      bool eq = false;
+      if (v < V && allowed(v)) {
+        const float s = score(v);
+        const uint32_t k = score_key(s);
+        if (k > prefix) take(v, s);
+        eq = k == prefix;
+      }
+      const uint64_t bal = __ballot(eq);
+      const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) red_i[wave] = __popcll(bal);
+      __syncthreads();
+      int before = s_run;
+      for (int w = 0; w < wave; ++w) before += red_i[w];
+      if (eq && before + before_in_wave < need) take(v, score(v));
+      __syncthreads();
+      if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < kWaves; ++w) tot += red_i[w];
+        s_run += tot;
+      }
+      __syncthreads();
+    }
+  }
+
+  // --- maximizer over the workgroup ----------------------------------------
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int32_t oi = __shfl_xor(bi, off);
+    merge_best(bv, bi, ov, oi);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    red_v[wave] = bv;
+    red_i[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = -INFINITY;
+    int32_t i = -1;
+    for (int w = 0; w < kWaves; ++w) merge_best(v, i, red_v[w], red_i[w]);
+    p.out_idx[b] = i;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Grouped combine: one thread per row.
 // ---------------------------------------------------------------------------
 __global__ void group_combine_kernel(const GroupSummary* __restrict__ s, int n_groups, int B, uint32_t seed_lo,
@@ -282,6 +489,11 @@ hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_tiles_kernel<EPI_FLAT>, dim3((p.B + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, p.B,
                      p.n_tiles, p.ws_val, p.ws_idx, nullptr, nullptr, p.out_idx, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_sample_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -68,21 +68,22 @@ def _sample_rows(B):
     return np.unique(np.array([0, B // 2, B - 1], np.int32))
 
 
-def _parity_run(fs, ctx, wl, B, T, steps, mask=None, seed=0):
+def _parity_run(fs, ctx, wl, B, T, steps, mask=None, seed=0, top_k=0):
     import torch
 
     H = synth.workload_H(wl.name, B=B)
     Hd = dev_bf16(H)
     md = None if mask is None else dev_words(mask)
-    say(f"{wl.name} B={B}: {steps} GPU steps")
-    outs = [fs.fs_fmms_sample(ctx, Hd, wl.Wd, T, seed, s, mask=md) for s in range(steps)]
+    say(f"{wl.name} B={B} top_k={top_k}: {steps} GPU steps")
+    outs = [fs.fs_fmms_sample(ctx, Hd, wl.Wd, T, seed, s, mask=md, top_k=top_k) for s in range(steps)]
     _sync()
     gpu = torch.stack(outs).cpu().numpy()
     rows = _sample_rows(B)
     say(f"{wl.name} B={B}: oracle logits for rows {rows.tolist()}")
     L = oracle.logits(H[rows], wl.W)
-    ora, _ = oracle.sample_rows_steps(L, rows, T, seed, 0, steps, mask=mask)
-    n = check_ids(gpu[:, rows], ora, oracle_p_fn(L, rows, T, seed, 0, mask=mask), f"{wl.name} B={B}")
+    ora, _ = oracle.sample_rows_steps(L, rows, T, seed, 0, steps, mask=mask, top_k=top_k)
+    n = check_ids(gpu[:, rows], ora, oracle_p_fn(L, rows, T, seed, 0, mask=mask, top_k=top_k),
+                  f"{wl.name} B={B} top_k={top_k}")
     say(f"{wl.name} B={B}: {steps}x{len(rows)} sampled rows, near-tie mismatches {n}")
     return gpu, H, L, rows
 
@@ -95,6 +96,16 @@ def test_small_decode_head(fs, ctx, small, B):
 @pytest.mark.parametrize("B", [1, 8, 32, 64, 128, 256])
 def test_mid_decode_head(fs, ctx, mid, B):
     _parity_run(fs, ctx, mid, B, 0.7, 100)
+
+
+@pytest.mark.parametrize("B", [8, 64])
+def test_mid_decode_head_topk50(fs, ctx, mid, B):
+    # the mid decode head's top-k variant: exact top-50 of the scores, then the
+    # Gumbel-max within them
+    gpu, _, L, rows = _parity_run(fs, ctx, mid, B, 0.7, 20, top_k=50)
+    for j, r in enumerate(rows):  # every draw lies in the oracle's top-50 set
+        kept = set(np.argsort(-L[j].astype(np.float64), kind="stable")[:50].tolist())
+        assert set(gpu[:, r].tolist()) <= kept
 
 
 def test_mid_decode_tile_maxima(fs, ctx, mid):

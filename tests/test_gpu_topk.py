@@ -1,0 +1,159 @@
+"""GPU parity of top-k sampling (exact top-k of the allowed scores, then the
+Gumbel-max over the kept ids) against the CPU oracle.
+
+The oracle is given the logits the GPU computed (read back from the unfused
+path's workspace), so both sides select the top-k set from identical fp32
+scores; the only remaining difference is the noise (fp32 on the GPU, fp64 in
+the oracle), which the near-tie rule covers.  Cases: tiny and ragged shapes,
+k = 1 (plain argmax of the scores), k >= the allowed count (no-op), exact ties
+across the k-th boundary (kept by lower id), masks, and boundaries wider than
+the selection kernel's candidate buffer (refinement levels and the in-order
+pass over equal keys).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import check_ids, dev_bf16, dev_words, oracle_p_fn, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fs():
+    import torch
+
+    import lm_head_matmul_amd as fs_mod
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return fs_mod
+
+
+@pytest.fixture(scope="module")
+def ctx(fs):
+    import torch
+
+    c = fs.fs_create(0, max_B=256, max_V=262144, max_top_k=5000)
+    torch.cuda.synchronize()
+    yield c
+    torch.cuda.synchronize()
+    fs.fs_destroy(c)
+
+
+def _gpu_logits(fs, ctx, Hd, Wd, B, V, path=0):
+    import torch
+
+    ws = torch.empty((B, (V + 3) // 4 * 4), dtype=torch.float32, device="cuda")
+    fs.fs_unfused_sample(ctx, Hd, Wd, 1.0, 0, 0, logits_ws=ws, path=path)
+    torch.cuda.synchronize()
+    return np.ascontiguousarray(ws.cpu().numpy()[:, :V])
+
+
+def _sample(fs, ctx, Hd, Wd, T, seed, steps, top_k, mask=None, path=0, unfused=False):
+    import torch
+
+    outs = []
+    for s in steps:
+        if unfused:
+            outs.append(fs.fs_unfused_sample(ctx, Hd, Wd, T, seed, s, mask=mask, top_k=top_k, path=path))
+        else:
+            outs.append(fs.fs_fmms_sample(ctx, Hd, Wd, T, seed, s, mask=mask, top_k=top_k, path=path))
+    torch.cuda.synchronize()
+    return torch.stack(outs).cpu().numpy()
+
+
+def _check(fs, ctx, H, W, T, seed, nsteps, top_k, mask_np=None, path=0, label=""):
+    B, V = H.shape[0], W.shape[0]
+    Hd, Wd = dev_bf16(H), dev_bf16(W)
+    md = None if mask_np is None else dev_words(mask_np)
+    L = _gpu_logits(fs, ctx, Hd, Wd, B, V, path)
+    fused = _sample(fs, ctx, Hd, Wd, T, seed, range(nsteps), top_k, md, path)
+    unfused = _sample(fs, ctx, Hd, Wd, T, seed, range(nsteps), top_k, md, path, unfused=True)
+    assert np.array_equal(fused, unfused), f"{label}: fused and unfused top-k differ"
+    rows = np.arange(B)
+    ora, _ = oracle.sample_rows_steps(L, rows, T, seed, 0, nsteps, mask=mask_np, top_k=top_k)
+    n = check_ids(fused, ora, oracle_p_fn(L, rows, T, seed, 0, mask=mask_np, top_k=top_k), label)
+    say(f"{label}: {n} near-tie mismatches over {fused.size} draws")
+    return fused, L
+
+
+@pytest.mark.parametrize("B,d,V,T,k,path", [
+    (4, 256, 4096, 1.0, 50, 0),
+    (4, 256, 4096, 1.0, 50, 2),
+    (8, 520, 3000, 0.7, 5, 0),
+    (3, 256, 1000, 1.0, 1000, 0),   # k = V: every id kept
+    (5, 264, 700, 1.3, 4999, 0),    # k > V
+    (20, 1024, 5000, 0.8, 64, 0),
+    (70, 264, 333, 1.0, 17, 0),     # more rows than one workspace chunk
+])
+def test_topk_parity(fs, ctx, B, d, V, T, k, path):
+    say(f"top-k parity B={B} d={d} V={V} T={T} k={k} path={path}")
+    H = synth.normal_bf16(B, d, seed=21)
+    W = synth.normal_bf16(V, d, seed=22, std=0.05)
+    _check(fs, ctx, H, W, T, 3, 20, k, path=path, label=f"topk k={k}")
+
+
+def test_topk_one_is_argmax(fs, ctx):
+    B, d, V = 6, 512, 2500
+    H = synth.normal_bf16(B, d, seed=23)
+    W = synth.normal_bf16(V, d, seed=24, std=0.05)
+    ids, L = _check(fs, ctx, H, W, 1.0, 4, 10, 1, label="k=1")
+    want = np.argmax(L, axis=1)  # numpy: first index of the maximum
+    assert np.all(ids == want[None, :])
+
+
+def test_topk_ties_at_boundary(fs, ctx):
+    # integer logits: many exactly equal scores, the k-th value falls inside a tie group
+    B, d, V, k = 6, 256, 3000, 40
+    H = synth.small_int_bf16(B, d, seed=25)
+    W = synth.small_int_bf16(V, d, seed=26, lo=-1, hi=1)
+    ids, L = _check(fs, ctx, H, W, 1.0, 5, 40, k, label="ties")
+    for b in range(B):  # every draw is one of the k lowest-id ids among the top scores
+        order = np.lexsort((np.arange(V), -L[b].astype(np.float64)))
+        kept = set(order[:k].tolist())
+        assert set(ids[:, b].tolist()) <= kept
+
+
+def test_topk_with_mask(fs, ctx):
+    B, d, V, k = 10, 520, 3000, 30
+    H = synth.normal_bf16(B, d, seed=27)
+    W = synth.outlier_bf16(V, d, 28, 29, 0.05, 0.5, 0.01)
+    allowed = np.random.default_rng(30).random((B, V)) >= 0.3
+    allowed[2] = False                   # nothing allowed: -1
+    allowed[3] = False
+    allowed[3, [5, 2999, 1400]] = True   # fewer allowed ids than k: all of them kept
+    mask = synth.pack_mask(allowed)
+    ids, _ = _check(fs, ctx, H, W, 1.0, 6, 20, k, mask_np=mask, label="masked top-k")
+    assert np.all(ids[:, 2] == -1)
+    assert set(ids[:, 3].tolist()) <= {5, 2999, 1400}
+    for b in range(B):
+        if b != 2:
+            assert np.all(allowed[b, ids[:, b]])
+
+
+def test_topk_all_scores_equal(fs, ctx):
+    # every score is 0: the boundary holds all V equal keys (more than the
+    # selection kernel gathers), so the k lowest ids are kept
+    B, d, V, k = 3, 256, 9000, 25
+    H = np.zeros((B, d), np.uint16)
+    W = synth.normal_bf16(V, d, seed=31)
+    ids, L = _check(fs, ctx, H, W, 1.0, 7, 30, k, label="all equal")
+    assert np.all(L == 0)
+    assert np.all((ids >= 0) & (ids < k))
+
+
+def test_topk_narrow_score_range(fs, ctx):
+    # scores within a few ulps of 1.0 for most ids: the first-level bin is too
+    # wide for the candidate buffer and the selection refines it
+    B, d, V, k = 2, 256, 12000, 50
+    H = np.zeros((B, d), np.uint16)
+    H[:, 0] = 0x3F80  # 1.0
+    W = np.zeros((V, d), np.uint16)
+    rng = np.random.default_rng(32)
+    W[:, 0] = 0x3F80 + rng.integers(0, 8, V).astype(np.uint16)  # 1.0 .. 1.0546875
+    W[::7, 0] = 0x3F00  # some far below (0.5)
+    ids, L = _check(fs, ctx, H, W, 1.0, 8, 30, k, label="narrow range")
+    for b in range(B):
+        order = np.lexsort((np.arange(V), -L[b].astype(np.float64)))
+        assert set(ids[:, b].tolist()) <= set(order[:k].tolist())
