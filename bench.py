@@ -90,7 +90,11 @@ PROFILE_CMDS = {
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write "
              "-- python3 bench.py --profile --steps 5 --warmup 2",
 }
-HEADLINE_KERNEL = "fmms_mfma_kernel"
+
+def headline_kernel_name(names):
+    """The streaming kernel of the step: the library's kernel with the largest total time."""
+    ours = [n for n in names if "fsk::" in n and "reduce_tiles" not in n]
+    return ours[0] if ours else None
 
 
 def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B=64):
@@ -103,11 +107,14 @@ def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B
     tag = f"{workload}_B{B}"
     pre = "cd /tmp && export TMPDIR=/tmp && cd <repo root> && "
 
-    stats = list(csv.DictReader(open(trace_csv)))
-    head = [r for r in stats if HEADLINE_KERNEL in r["Name"]]
-    assert len(head) == 1, "expected one headline kernel instance in the trace"
+    stats = sorted(csv.DictReader(open(trace_csv)), key=lambda r: -float(r["TotalDurationNs"]))
+    kname = headline_kernel_name([r["Name"] for r in stats])
+    assert kname is not None, "no library kernel in the trace"
+    head = [r for r in stats if r["Name"] == kname]
     avg_us = float(head[0]["AverageNs"]) / 1e3
-    lines = [f"# {HEADLINE_KERNEL}: {workload} head (B={B}, d={w['d']}, V={w['V']}), kernel trace", "",
+    short = kname.split("(")[0].split("::")[-1].split("<")[0]
+    lines = [f"# {short}: {workload} head (B={B}, d={w['d']}, V={w['V']}), kernel trace", "",
+             f"headline kernel: `{kname}`", "",
              f"command: `{pre}{PROFILE_CMDS['trace']}`", "",
              "The run: one 1 GiB device fill and copy (counter calibration), 50 warmup and 1000 timed steps.", "",
              "| kernel | calls | average us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|"]
@@ -118,7 +125,7 @@ def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B
               f"- algorithmic_bytes_per_launch: {algo}",
               f"- achieved_GB_per_s_at_trace_average: {algo / (avg_us * 1e-6) / 1e9:.1f}",
               f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
-    path = os.path.join(ROOT, "profiles", f"{HEADLINE_KERNEL}_{tag}_kernel_trace.md")
+    path = os.path.join(ROOT, "profiles", f"{short}_{tag}_kernel_trace.md")
     open(path, "w").write("\n".join(lines))
 
     def rows(fn):
@@ -134,11 +141,13 @@ def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B
     fr, wr = rows(fetch_csv), rows(write_csv)
     f_fac, f_cal = calib(fr, "FETCH_SIZE")
     w_fac, w_cal = calib(wr, "WRITE_SIZE")
-    f_k = [float(r["Counter_Value"]) for r in fr if HEADLINE_KERNEL in r["Kernel_Name"]]
-    w_k = [float(r["Counter_Value"]) for r in wr if HEADLINE_KERNEL in r["Kernel_Name"]]
+    f_k = [float(r["Counter_Value"]) for r in fr if r["Kernel_Name"] == kname]
+    w_k = [float(r["Counter_Value"]) for r in wr if r["Kernel_Name"] == kname]
+    assert f_k and w_k, "the headline kernel is missing from a counter pass"
     f_kib, w_kib = sum(f_k) / len(f_k), sum(w_k) / len(w_k)
     hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
-    lines = [f"# {HEADLINE_KERNEL}: {workload} head (B={B}, d={w['d']}, V={w['V']}), HBM traffic per launch", "",
+    lines = [f"# {short}: {workload} head (B={B}, d={w['d']}, V={w['V']}), HBM traffic per launch", "",
+             f"kernel: `{kname}`", "",
              f"fetch pass: `{pre}{PROFILE_CMDS['fetch']}`", "",
              f"write pass: `{pre}{PROFILE_CMDS['write']}`", "",
              "Calibration: the same runs first fill 1 GiB (a pure write) and copy it (a 1 GiB read + write).",
@@ -303,6 +312,33 @@ def main():
                 log(f"sweep {sweep[-1]}")
             del weights[name]
             torch.cuda.empty_cache()
+        # the mid decode head's top-k variant (k = 50)
+        wt = synth.WORKLOADS["mid_decode"]
+        for b in (8, 64):
+            _, Wt = load_W("mid_decode")
+            Ht = H_for("mid_decode", b)
+            outt = torch.empty(b, dtype=torch.int32, device=dev)
+            lgt = torch.empty((b, (wt["V"] + 3) // 4 * 4), dtype=torch.float32, device=dev)
+
+            def tk(i, base, unf):
+                if unf:
+                    fs.fs_unfused_sample(ctx, Ht, Wt[i % len(Wt)], wt["T"], 0, base + i, top_k=50, out=outt,
+                                         logits_ws=lgt)
+                else:
+                    fs.fs_fmms_sample(ctx, Ht, Wt[i % len(Wt)], wt["T"], 0, base + i, top_k=50, out=outt)
+
+            timer.run(lambda i: tk(i, 0, False), 5)
+            k_ms, _ = timer.run(lambda i: tk(i, 10, False), max(20, n // 4))
+            timer.run(lambda i: tk(i, 0, True), 5)
+            ku_ms, _ = timer.run(lambda i: tk(i, 10, True), max(20, n // 4))
+            ab = algorithmic_bytes(b, wt["d"], wt["V"])
+            sweep.append({"workload": "mid_decode_top50", "B": b, "d": wt["d"], "V": wt["V"], "top_k": 50,
+                          "us_per_step": round(k_ms * 1e3, 2), "GB_per_s": round(ab / (k_ms * 1e-3) / 1e9, 1),
+                          "pct_peak": round(100 * ab / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                          "unfused_us_per_step": round(ku_ms * 1e3, 2)})
+            log(f"sweep {sweep[-1]}")
+        del weights["mid_decode"]
+        torch.cuda.empty_cache()
         # masked workload
         wm = synth.WORKLOADS["masked"]
         mask = torch.from_numpy(synth.workload_mask("masked").view(np.int32)).to(dev)

@@ -30,6 +30,13 @@ struct fs_ctx {
   float* topk_ws;
   int64_t topk_ldl;
   int topk_rows;
+  // top-k selection workspace for topk_rows rows (see fsk::TopkParams)
+  void* topk_sel;
+  uint32_t* topk_hist;
+  uint64_t* topk_cand;
+  int32_t* topk_cand_n;
+  float* topk_seg_val;
+  int32_t* topk_seg_idx;
 };
 
 namespace {
@@ -189,13 +196,12 @@ int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t str
 
 // Top-k sampling of batch rows [r0, r0 + rows) whose unscaled logits are in
 // logits (row r0 first).
-int launch_topk(const float* logits, int64_t ldl, int rows, int r0, int64_t V, float temperature, uint64_t seed,
-                uint64_t step, const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, hipStream_t s) {
+int launch_topk(const fs_ctx* ctx, const float* logits, int64_t ldl, int rows, int r0, int64_t V, float temperature,
+                uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx,
+                hipStream_t s) {
   fsk::TopkParams q;
   std::memset(&q, 0, sizeof q);
-  q.logits = logits;
   q.ldl = ldl;
-  q.B = rows;
   q.V = (int)V;
   q.inv_t = 1.0f / temperature;
   q.seed_lo = (uint32_t)seed;
@@ -204,11 +210,30 @@ int launch_topk(const float* logits, int64_t ldl, int rows, int r0, int64_t V, f
   q.step_hi = (uint32_t)(step >> 32);
   q.mask = mask;
   q.ldm = ldm;
-  q.row_offset = r0;
   q.top_k = top_k;
-  q.out_idx = out_idx + r0;
-  hipError_t e = fsk::launch_topk_sample(q, s);
-  if (e != hipSuccess) return hip_fail(e, "top-k sampling kernel launch");
+  q.hist = ctx->topk_hist;
+  q.cand = ctx->topk_cand;
+  q.cand_n = ctx->topk_cand_n;
+  q.seg_val = ctx->topk_seg_val;
+  q.seg_idx = ctx->topk_seg_idx;
+  // rows are processed in chunks of the workspace's topk_rows; each row is split
+  // into segments so that a chunk launches about 2048 workgroups, with segments
+  // of at least 512 quads
+  for (int c0 = 0; c0 < rows; c0 += ctx->topk_rows) {
+    const int n = (rows - c0) < ctx->topk_rows ? (rows - c0) : ctx->topk_rows;
+    const int64_t nq = (V + 3) / 4;
+    int64_t seg = 2048 / n;
+    if (seg > nq / 512) seg = nq / 512;
+    if (seg > fsk::kTopkMaxSeg) seg = fsk::kTopkMaxSeg;
+    if (seg < 1) seg = 1;
+    q.logits = logits + (int64_t)c0 * ldl;
+    q.B = n;
+    q.row_offset = r0 + c0;
+    q.out_idx = out_idx + r0 + c0;
+    q.n_seg = (int)seg;
+    hipError_t e = fsk::launch_topk_sample(q, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k sampling kernel launch");
+  }
   return FS_OK;
 }
 
@@ -270,6 +295,27 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
       delete c;
       return hip_fail(e, "hipMalloc(top-k workspace)");
     }
+    // selection workspace: cand [rows][cap] u64, hist [rows][bins] u32, seg_val / seg_idx
+    // [rows][max_seg], cand_n [rows]; hist and cand_n start at zero and every call
+    // leaves them at zero
+    const size_t R = (size_t)c->topk_rows;
+    const size_t sel = R * fsk::kTopkCap * 8 + R * fsk::kTopkBins * 4 + R * fsk::kTopkMaxSeg * 8 + R * 4;
+    e = hipMalloc(&c->topk_sel, sel);
+    if (e == hipSuccess) e = hipMemset(c->topk_sel, 0, sel);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      if (c->topk_sel) (void)hipFree(c->topk_sel);
+      (void)hipFree(c->topk_ws);
+      (void)hipFree(c->base);
+      delete c;
+      return hip_fail(e, "top-k selection workspace");
+    }
+    char* t = (char*)c->topk_sel;
+    c->topk_cand = (uint64_t*)t;
+    c->topk_hist = (uint32_t*)(t + R * fsk::kTopkCap * 8);
+    c->topk_seg_val = (float*)(t + R * fsk::kTopkCap * 8 + R * fsk::kTopkBins * 4);
+    c->topk_seg_idx = (int32_t*)(c->topk_seg_val + R * fsk::kTopkMaxSeg);
+    c->topk_cand_n = (int32_t*)(c->topk_seg_idx + R * fsk::kTopkMaxSeg);
   }
   *out = c;
   return FS_OK;
@@ -280,6 +326,7 @@ void fs_destroy(fs_ctx* ctx) {
   DeviceGuard guard(ctx->device);
   if (ctx->base) (void)hipFree(ctx->base);
   if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
+  if (ctx->topk_sel) (void)hipFree(ctx->topk_sel);
   delete ctx;
 }
 
@@ -317,7 +364,7 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
   if (top_k > 0) {
     // The exact top-k boundary of a row needs all of its scores: the streaming
     // pass stores them into the context's workspace (batch chunks of
-    // topk_rows rows) and a per-row selection kernel samples the kept set.
+    // topk_rows rows) and the selection launches sample the kept set.
     hipStream_t s = (hipStream_t)stream;
     for (int r0 = 0; r0 < B; r0 += ctx->topk_rows) {
       const int Bc = (B - r0) < ctx->topk_rows ? (B - r0) : ctx->topk_rows;
@@ -327,7 +374,7 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
         c.ldl = ctx->topk_ldl;
       });
       if (rc != FS_OK) return rc;
-      rc = launch_topk(ctx->topk_ws, ctx->topk_ldl, Bc, r0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
+      rc = launch_topk(ctx, ctx->topk_ws, ctx->topk_ldl, Bc, r0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
       if (rc != FS_OK) return rc;
     }
     return FS_OK;
@@ -363,7 +410,7 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
     c.ldl = ldl;
   });
   if (rc != FS_OK) return rc;
-  if (top_k > 0) return launch_topk(logits_ws, ldl, B, 0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
+  if (top_k > 0) return launch_topk(ctx, logits_ws, ldl, B, 0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
   fsk::SampleParams q;
   std::memset(&q, 0, sizeof q);
   q.logits = logits_ws;

@@ -70,7 +70,8 @@ struct SampleParams {  // unfused second pass: sample from stored logits
   int32_t* out_idx;
 };
 
-// Top-k sampling from stored fp32 logits, one workgroup per batch row.
+// Top-k sampling from stored fp32 logits (segment-parallel radix select, then a
+// per-row finish).
 struct TopkParams {
   const float* logits;  // [B][ldl], row b holds global batch row row_offset + b
   int64_t ldl;
@@ -83,6 +84,13 @@ struct TopkParams {
   int row_offset;
   int top_k;
   int32_t* out_idx;  // [B]
+  // selection workspace, zero between calls where noted
+  int n_seg;           // segments per row (<= kTopkMaxSeg)
+  uint32_t* hist;      // [B][kTopkBins] row histograms of key bits 31..20 (zero)
+  uint64_t* cand;      // [B][kTopkCap] boundary-bin candidates (key << 32 | ~id)
+  int32_t* cand_n;     // [B] candidate counts (zero)
+  float* seg_val;      // [B][kTopkMaxSeg] segment maximizers
+  int32_t* seg_idx;
 };
 
 // Kernel selection for a streaming launch.
@@ -105,6 +113,9 @@ constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exa
 constexpr int kMfmaMaxB = 64;
 constexpr int kKouterMaxRounds = 5;  // accumulator sets a wave keeps in registers in the chunk-outer kernel
 constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
+constexpr int kTopkBins = 4096;    // first-level bins of the top-k radix select (key bits 31..20)
+constexpr int kTopkCap = 4096;     // boundary-bin ids the segment-parallel selection gathers per row
+constexpr int kTopkMaxSeg = 64;    // segments per row in the top-k launches
 
 // Mask words per row staged for the largest tile of a launch.
 inline int64_t tile_mask_words(int64_t n_mblocks, int n_tiles) {

@@ -64,192 +64,80 @@ __global__ void __launch_bounds__(kThreads) sample_logits_kernel(const SamplePar
 }
 
 // ---------------------------------------------------------------------------
-// Top-k sampling from stored logits.  Per row (one workgroup): exact top-k of
-// the allowed scores s = logit * (1/T) by a most-significant-digit radix
-// select on order-preserving 32-bit keys, ties at the boundary kept by lower
-// id; then the Gumbel-max over the kept ids.  [readus.org FlashSampling
-// summary, section on Top-K and masking: the sampler acts on the kept set]
+// Top-k sampling from stored logits: exact top-k of the allowed scores
+// s = logit * (1/T), ties at the boundary kept by lower id, then the
+// Gumbel-max over the kept ids.  [readus.org FlashSampling summary, section on
+// Top-K and masking: the sampler acts on the kept set]
 //
-//   level 0 histogram of key bits 31..20 over the row; the bin where the count
-//   from the top reaches k is the boundary; keys in higher bins are kept.
-//   If the boundary bin holds at most kTopkCap keys they are gathered into
-//   LDS and sorted by (key desc, id asc); else the bin is refined on bits
-//   19..8 and 7..0.  A boundary of more than kTopkCap equal keys is resolved
-//   by a pass in id order.
+// Keys are order-preserving 32-bit images of the scores; the boundary is found
+// by a most-significant-digit radix select whose first level histograms key
+// bits 31..20.  Three launches per batch chunk, each row split into segments:
+//   1. histogram: every (segment, row) workgroup counts its keys in LDS and adds
+//      the non-zero bins into the row's histogram in global memory;
+//   2. collect: every (segment, row) workgroup reads the row's histogram, finds
+//      the boundary bin (the bin where the count from the top reaches k), takes
+//      the Gumbel-max over its ids above that bin, and appends its ids inside
+//      the bin to the row's candidate list;
+//   3. finish, one workgroup per row: sorts the candidates by (key desc, id asc),
+//      perturbs the first k - (count above) of them and merges them with the
+//      segments' maximizers; it then clears the row's histogram and count for
+//      the next call.
+// A boundary bin holding more than kTopkCap ids (very narrow score ranges) is
+// resolved by the finish workgroup alone: it refines the bin on key bits 19..8
+// and 7..0 and, if more than kTopkCap ids share the exact boundary key, keeps
+// the lowest of them by a pass in id order.
 // ---------------------------------------------------------------------------
-constexpr int kTopkCap = 4096;
-
 // Order-preserving key of a score, with -0 folded onto +0 (they compare equal).
 __device__ __forceinline__ uint32_t score_key(float x) {
   const uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ void __launch_bounds__(kThreads) topk_sample_kernel(const TopkParams p) {
-  __shared__ uint32_t hist[4096];
-  __shared__ uint64_t cand[kTopkCap];
-  __shared__ int s_bin, s_above, s_inbin, s_total, s_ncand, s_run;
-  __shared__ float red_v[kWaves];
-  __shared__ int32_t red_i[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x;
-  const float* L = p.logits + (int64_t)b * p.ldl;
-  const uint32_t grow = (uint32_t)(p.row_offset + b);
-  const uint32_t* M = p.mask ? p.mask + (int64_t)grow * p.ldm : nullptr;
-  const int V = p.V;
-  auto allowed = [&](int v) { return M == nullptr || ((M[v >> 5] >> (v & 31)) & 1u); };
-  auto score = [&](int v) { return L[v] * p.inv_t; };
+struct TopkShared {
+  uint32_t hist[kTopkBins];
+  uint64_t cand[kTopkCap];
+  int bin, above, inbin, total, ncand, run;
+  float red_v[kWaves];
+  int32_t red_i[kWaves];
+};
 
-  float bv = -INFINITY;
-  int32_t bi = -1;
-  auto take = [&](int v, float s) {  // kept id: perturb and update the maximizer
-    const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)v >> 2, grow, p.step_lo, p.step_hi);
-    const uint32_t q = (uint32_t)v & 3u;
-    const uint32_t w = q == 0 ? r.w[0] : q == 1 ? r.w[1] : q == 2 ? r.w[2] : r.w[3];
-    merge_best(bv, bi, s + gumbel_from_bits(w), v);
-  };
-
-  // --- radix select of the boundary ---------------------------------------
-  uint32_t prefix = 0, pmask = 0;
-  int need = p.top_k;
-  bool keep_all = false;
-  int shift = 20, nbins = 4096;
-  int level = 0;
-  for (; level < 3; ++level) {
-    for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int v = tid; v < V; v += kThreads) {
-      if (!allowed(v)) continue;
-      const uint32_t k = score_key(score(v));
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins [hi - (l + 1) * per, hi - l * per) counted from the top
-      const int per = nbins / 64;
-      const int top = nbins - 1 - lane * per;
-      int local = 0;
-      for (int j = 0; j < per; ++j) local += (int)hist[top - j];
-      int incl = local;  // inclusive prefix over lanes 0..lane (from the top)
+// Wave 0: the boundary of a histogram of nbins bins (counts from the top):
+// total count, the bin where the running count from the top reaches `need`,
+// the count above that bin and the count inside it.  If total < need the bin
+// fields are left unset.
+__device__ __forceinline__ void topk_boundary(const uint32_t* h, int nbins, int need, TopkShared& sh) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbins / 64;  // lane l owns bins [hi - (l + 1) * per, hi - l * per) counted from the top
+  const int top = nbins - 1 - lane * per;
+  int local = 0;
+  for (int j = 0; j < per; ++j) local += (int)h[top - j];
+  int incl = local;  // inclusive prefix over lanes 0..lane
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      const int excl = incl - local;
-      const int total = __shfl(incl, 63);
-      if (lane == 0) s_total = total;
-      if (excl < need && incl >= need) {  // the boundary lies in this lane's bins
-        int run = excl;
-        for (int j = 0; j < per; ++j) {
-          const int c = (int)hist[top - j];
-          if (run + c >= need) {
-            s_bin = top - j;
-            s_above = run;
-            s_inbin = c;
-            break;
-          }
-          run += c;
-        }
-      }
-    }
-    __syncthreads();
-    if (level == 0 && s_total <= need) {  // no more allowed ids than k: keep them all
-      keep_all = true;
-      break;
-    }
-    need -= s_above;
-    prefix |= (uint32_t)s_bin << shift;
-    pmask |= (uint32_t)(nbins - 1) << shift;
-    if (s_inbin <= kTopkCap) break;
-    if (level == 0) {
-      shift = 8;
-      nbins = 4096;
-    } else {
-      shift = 0;
-      nbins = 256;
-    }
-    __syncthreads();  // s_* are rewritten by the next level
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  const bool gather = keep_all || level < 3;
-
-  // --- kept ids above the boundary; boundary candidates into LDS ------------
-  if (tid == 0) s_ncand = 0;
-  __syncthreads();
-  if (gather) {
-    for (int v = tid; v < V; v += kThreads) {
-      if (!allowed(v)) continue;
-      const float s = score(v);
-      const uint32_t k = score_key(s);
-      const uint32_t hi = k & pmask;
-      if (keep_all || hi > prefix) {
-        take(v, s);
-      } else if (hi == prefix) {
-        const int at = atomicAdd(&s_ncand, 1);
-        cand[at] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+  const int excl = incl - local;
+  const int total = __shfl(incl, 63);
+  if (lane == 0) sh.total = total;
+  if (excl < need && incl >= need) {
+    int run = excl;
+    for (int j = 0; j < per; ++j) {
+      const int c = (int)h[top - j];
+      if (run + c >= need) {
+        sh.bin = top - j;
+        sh.above = run;
+        sh.inbin = c;
+        break;
       }
-    }
-    __syncthreads();
-    if (!keep_all) {
-      // bitonic sort, descending, of the candidates (padded with zeros)
-      const int n = s_ncand;
-      int np2 = 1;
-      while (np2 < n) np2 <<= 1;
-      for (int i = n + tid; i < np2; i += kThreads) cand[i] = 0;
-      __syncthreads();
-      for (int kk = 2; kk <= np2; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-          for (int i = tid; i < np2; i += kThreads) {
-            const int ij = i ^ j;
-            if (ij > i) {
-              const uint64_t x = cand[i], y = cand[ij];
-              const bool desc = (i & kk) == 0;
-              if (desc ? (x < y) : (x > y)) {
-                cand[i] = y;
-                cand[ij] = x;
-              }
-            }
-          }
-          __syncthreads();
-        }
-      }
-      for (int i = tid; i < need && i < n; i += kThreads) {
-        const int v = (int)(0xFFFFFFFFu - (uint32_t)(cand[i] & 0xFFFFFFFFu));
-        take(v, score(v));
-      }
-    }
-  } else {
-    // more than kTopkCap ids share the exact boundary key: keys above it are
-    // kept, and of those equal to it the `need` lowest ids, found in id order
-    if (tid == 0) s_run = 0;
-    __syncthreads();
-    for (int base = 0; base < V; base += kThreads) {
-      const int v = base + tid;
-      bool eq = false;
-      if (v < V && allowed(v)) {
-        const float s = score(v);
-        const uint32_t k = score_key(s);
-        if (k > prefix) take(v, s);
-        eq = k == prefix;
-      }
-      const uint64_t bal = __ballot(eq);
-      const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) red_i[wave] = __popcll(bal);
-      __syncthreads();
-      int before = s_run;
-      for (int w = 0; w < wave; ++w) before += red_i[w];
-      if (eq && before + before_in_wave < need) take(v, score(v));
-      __syncthreads();
-      if (tid == 0) {
-        int tot = 0;
-        for (int w = 0; w < kWaves; ++w) tot += red_i[w];
-        s_run += tot;
-      }
-      __syncthreads();
+      run += c;
     }
   }
+}
 
-  // --- maximizer over the workgroup ----------------------------------------
+// Workgroup maximizer; the result is valid in thread 0.
+__device__ __forceinline__ void topk_block_best(float& bv, int32_t& bi, TopkShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(bv, off);
@@ -258,16 +146,285 @@ __global__ void __launch_bounds__(kThreads) topk_sample_kernel(const TopkParams 
   }
   __syncthreads();
   if (lane == 0) {
-    red_v[wave] = bv;
-    red_i[wave] = bi;
+    sh.red_v[wave] = bv;
+    sh.red_i[wave] = bi;
   }
   __syncthreads();
-  if (tid == 0) {
-    float v = -INFINITY;
-    int32_t i = -1;
-    for (int w = 0; w < kWaves; ++w) merge_best(v, i, red_v[w], red_i[w]);
-    p.out_idx[b] = i;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < kWaves; ++w) merge_best(bv, bi, sh.red_v[w], sh.red_i[w]);
+}
+
+// Row view shared by the three launches.
+struct TopkRow {
+  const float* L;
+  const uint32_t* M;
+  uint32_t grow;
+  int V;
+  float inv_t;
+  __device__ bool allowed(int v) const { return M == nullptr || ((M[v >> 5] >> (v & 31)) & 1u); }
+  __device__ float score(int v) const { return L[v] * inv_t; }
+};
+
+__device__ __forceinline__ TopkRow topk_row(const TopkParams& p, int b) {
+  TopkRow r;
+  r.L = p.logits + (int64_t)b * p.ldl;
+  r.grow = (uint32_t)(p.row_offset + b);
+  r.M = p.mask ? p.mask + (int64_t)r.grow * p.ldm : nullptr;
+  r.V = p.V;
+  r.inv_t = p.inv_t;
+  return r;
+}
+
+// Perturb a kept id and update the maximizer.
+__device__ __forceinline__ void topk_take(const TopkParams& p, const TopkRow& row, int v, float s, float& bv,
+                                          int32_t& bi) {
+  const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)v >> 2, row.grow, p.step_lo, p.step_hi);
+  const uint32_t q = (uint32_t)v & 3u;
+  const uint32_t w = q == 0 ? r.w[0] : q == 1 ? r.w[1] : q == 2 ? r.w[2] : r.w[3];
+  merge_best(bv, bi, s + gumbel_from_bits(w), v);
+}
+
+// Visits the allowed ids of quads [q_lo, q_hi) of a row, four quads per
+// thread in flight: f(v, s, key).
+template <class F>
+__device__ __forceinline__ void topk_scan(const TopkRow& row, int64_t q_lo, int64_t q_hi, F&& f) {
+  constexpr int U = 4;
+  for (int64_t q0 = q_lo + threadIdx.x; q0 < q_hi; q0 += U * kThreads) {
+    f32x4_t x[U];
+    uint32_t bits[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t q = q0 + (int64_t)u * kThreads;
+      bits[u] = 0;
+      if (q < q_hi) {
+        const int v0 = (int)(q * 4);
+        x[u] = *(const f32x4_t*)(row.L + v0);  // rows are padded to whole quads
+        bits[u] = row.M ? (row.M[v0 >> 5] >> (uint32_t)(v0 & 31)) & 0xFu : 0xFu;
+        const int left = row.V - v0;
+        if (left < 4) bits[u] &= (1u << left) - 1u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v0 = (int)((q0 + (int64_t)u * kThreads) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((bits[u] >> i) & 1u) {
+          const float s = x[u][i] * row.inv_t;
+          f(v0 + i, s, score_key(s));
+        }
+    }
   }
+}
+
+__device__ __forceinline__ void topk_segment(const TopkParams& p, int seg, int64_t& q_lo, int64_t& q_hi) {
+  const int64_t nq = (p.V + 3) / 4;
+  q_lo = (int64_t)seg * nq / p.n_seg;
+  q_hi = (int64_t)(seg + 1) * nq / p.n_seg;
+}
+
+__global__ void __launch_bounds__(kThreads) topk_hist_kernel(const TopkParams p) {
+  __shared__ uint32_t hist[kTopkBins];
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const TopkRow row = topk_row(p, b);
+  for (int i = threadIdx.x; i < kTopkBins; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  int64_t q_lo, q_hi;
+  topk_segment(p, seg, q_lo, q_hi);
+  topk_scan(row, q_lo, q_hi, [&](int, float, uint32_t key) { atomicAdd(&hist[key >> 20], 1u); });
+  __syncthreads();
+  uint32_t* gh = p.hist + (int64_t)b * kTopkBins;
+  for (int i = threadIdx.x; i < kTopkBins; i += kThreads)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+__global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams p) {
+  __shared__ TopkShared sh;
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const TopkRow row = topk_row(p, b);
+  if (threadIdx.x < 64) topk_boundary(p.hist + (int64_t)b * kTopkBins, kTopkBins, p.top_k, sh);
+  __syncthreads();
+  const bool keep_all = sh.total <= p.top_k;
+  const uint32_t bin = keep_all ? 0u : (uint32_t)sh.bin;
+  const bool collect = !keep_all && sh.inbin <= kTopkCap;
+  float bv = -INFINITY;
+  int32_t bi = -1;
+  int64_t q_lo, q_hi;
+  topk_segment(p, seg, q_lo, q_hi);
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  // this segment's boundary candidates go to LDS first (at most the bin's count,
+  // <= kTopkCap), then to the row's list with one global atomic per workgroup
+  topk_scan(row, q_lo, q_hi, [&](int v, float s, uint32_t key) {
+    const uint32_t hi = key >> 20;
+    if (keep_all || hi > bin) {
+      topk_take(p, row, v, s, bv, bi);
+    } else if (collect && hi == bin) {
+      const int at = atomicAdd(&sh.ncand, 1);
+      sh.cand[at] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+    }
+  });
+  topk_block_best(bv, bi, sh);  // its barriers also publish sh.ncand and sh.cand
+  const int n = sh.ncand;
+  if (threadIdx.x == 0) {
+    p.seg_val[(int64_t)b * kTopkMaxSeg + seg] = bv;
+    p.seg_idx[(int64_t)b * kTopkMaxSeg + seg] = bi;
+    sh.run = n > 0 ? atomicAdd(&p.cand_n[b], n) : 0;
+  }
+  __syncthreads();
+  uint64_t* cand = p.cand + (int64_t)b * kTopkCap + sh.run;
+  for (int i = threadIdx.x; i < n; i += kThreads) cand[i] = sh.cand[i];
+}
+
+// Sorts sh.cand[0, n) descending (bitonic, padded with zeros to a power of 2).
+__device__ __forceinline__ void topk_sort_desc(TopkShared& sh, int n) {
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  for (int i = n + (int)threadIdx.x; i < np2; i += kThreads) sh.cand[i] = 0;
+  __syncthreads();
+  for (int kk = 2; kk <= np2; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < np2; i += kThreads) {
+        const int ij = i ^ j;
+        if (ij > i) {
+          const uint64_t x = sh.cand[i], y = sh.cand[ij];
+          const bool desc = (i & kk) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            sh.cand[i] = y;
+            sh.cand[ij] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int cand_id(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFu)); }
+
+// The whole selection for one row by one workgroup (boundary bins wider than
+// kTopkCap): the maximizer over the kept ids, valid in every thread's (bv, bi)
+// after the caller's block reduction.
+__device__ void topk_row_alone(const TopkParams& p, const TopkRow& row, TopkShared& sh, float& bv, int32_t& bi) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int V = row.V;
+  uint32_t prefix = 0, pmask = 0;
+  int need = p.top_k;
+  int shift = 20, nbins = kTopkBins;
+  int level = 0;
+  for (; level < 3; ++level) {
+    for (int i = tid; i < nbins; i += kThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int v = tid; v < V; v += kThreads) {
+      if (!row.allowed(v)) continue;
+      const uint32_t k = score_key(row.score(v));
+      if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) topk_boundary(sh.hist, nbins, need, sh);
+    __syncthreads();
+    need -= sh.above;
+    prefix |= (uint32_t)sh.bin << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    if (sh.inbin <= kTopkCap) break;
+    if (level == 0) {
+      shift = 8;
+      nbins = 4096;
+    } else {
+      shift = 0;
+      nbins = 256;
+    }
+    __syncthreads();  // the boundary fields are rewritten by the next level
+  }
+  if (level < 3) {
+    // kept ids above the boundary; boundary candidates into LDS, sorted
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+    for (int v = tid; v < V; v += kThreads) {
+      if (!row.allowed(v)) continue;
+      const float s = row.score(v);
+      const uint32_t k = score_key(s);
+      const uint32_t hi = k & pmask;
+      if (hi > prefix) {
+        topk_take(p, row, v, s, bv, bi);
+      } else if (hi == prefix) {
+        const int at = atomicAdd(&sh.ncand, 1);
+        sh.cand[at] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+      }
+    }
+    __syncthreads();
+    const int n = sh.ncand;
+    topk_sort_desc(sh, n);
+    for (int i = tid; i < need && i < n; i += kThreads) {
+      const int v = cand_id(sh.cand[i]);
+      topk_take(p, row, v, row.score(v), bv, bi);
+    }
+  } else {
+    // more than kTopkCap ids share the exact boundary key: keys above it are
+    // kept, and of those equal to it the `need` lowest ids, found in id order
+    if (tid == 0) sh.run = 0;
+    __syncthreads();
+    for (int base = 0; base < V; base += kThreads) {
+      const int v = base + tid;
+      bool eq = false;
+      if (v < V && row.allowed(v)) {
+        const float s = row.score(v);
+        const uint32_t k = score_key(s);
+        if (k > prefix) topk_take(p, row, v, s, bv, bi);
+        eq = k == prefix;
+      }
+      const uint64_t bal = __ballot(eq);
+      const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) sh.red_i[wave] = __popcll(bal);
+      __syncthreads();
+      int before = sh.run;
+      for (int w = 0; w < wave; ++w) before += sh.red_i[w];
+      if (eq && before + before_in_wave < need) topk_take(p, row, v, row.score(v), bv, bi);
+      __syncthreads();
+      if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < kWaves; ++w) tot += sh.red_i[w];
+        sh.run += tot;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) topk_finish_kernel(const TopkParams p) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const TopkRow row = topk_row(p, b);
+  uint32_t* gh = p.hist + (int64_t)b * kTopkBins;
+  if (tid < 64) topk_boundary(gh, kTopkBins, p.top_k, sh);
+  __syncthreads();
+  const bool keep_all = sh.total <= p.top_k;
+  const int need = keep_all ? 0 : p.top_k - sh.above;
+  const int inbin = keep_all ? 0 : sh.inbin;
+  float bv = -INFINITY;
+  int32_t bi = -1;
+  if (keep_all || inbin <= kTopkCap) {
+    for (int i = tid; i < p.n_seg; i += kThreads)
+      merge_best(bv, bi, p.seg_val[(int64_t)b * kTopkMaxSeg + i], p.seg_idx[(int64_t)b * kTopkMaxSeg + i]);
+    if (!keep_all) {
+      const uint64_t* cand = p.cand + (int64_t)b * kTopkCap;
+      for (int i = tid; i < inbin; i += kThreads) sh.cand[i] = cand[i];
+      topk_sort_desc(sh, inbin);  // begins with a barrier-separated fill
+      for (int i = tid; i < need; i += kThreads) {
+        const int v = cand_id(sh.cand[i]);
+        topk_take(p, row, v, row.score(v), bv, bi);
+      }
+    }
+  } else {
+    topk_row_alone(p, row, sh, bv, bi);
+  }
+  topk_block_best(bv, bi, sh);
+  if (tid == 0) {
+    p.out_idx[b] = bi;
+    p.cand_n[b] = 0;
+  }
+  for (int i = tid; i < kTopkBins; i += kThreads) gh[i] = 0;  // wave 0 read it before the barriers above
 }
 
 // ---------------------------------------------------------------------------
@@ -493,7 +650,10 @@ hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_sample_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
+  const dim3 grid(p.n_seg, p.B);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
