@@ -111,7 +111,12 @@ constexpr int kDotMaxB = 2;
 constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
 constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
-constexpr int kKouterMaxRounds = 5;  // accumulator sets a wave keeps in registers in the chunk-outer kernel
+// Rounds per pass of the chunk-outer kernel (accumulator sets a wave keeps in
+// registers): the most that fit 256 VGPRs without spilling, by epilogue, batch
+// blocks and masking.
+constexpr int kouter_max_rounds(int epi, int nb, bool masked) {
+  return (nb <= 2 || epi == EPI_STORE) ? 5 : (epi == EPI_FLAT && !masked) ? 3 : 2;
+}
 constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
 constexpr int kTopkBins = 4096;    // first-level bins of the top-k radix select (key bits 31..20)
 constexpr int kTopkCap = 4096;     // boundary-bin ids the segment-parallel selection gathers per row

@@ -599,11 +599,12 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   else
     cfg.fast = full_k && p.cs == kFastRingChunked && p.nbuf == 2 && p.nsub % kFastRingChunked == 0;
   // Chunked H with the fast driver: the chunk-outer kernel, whose passes cover
-  // up to kKouterMaxRounds rounds (one pass for most tiles).
+  // up to kouter_max_rounds rounds.
   cfg.rm = 0;
   if (!cfg.dot && cfg.fast && p.nchunk > 1) {
     const int64_t rounds = (tile_rows / 16 + kWaves - 1) / kWaves;
-    cfg.rm = (int)(rounds < kKouterMaxRounds ? rounds : kKouterMaxRounds);
+    const int cap = kouter_max_rounds(epi, cfg.nb, epi != EPI_STORE && p.mask != nullptr);
+    cfg.rm = (int)(rounds < cap ? rounds : cap);
   }
   if (!cfg.dot && cfg.fast && cfg.rm == 0 && epi != EPI_STORE) {
     const int pitch = (int)tile_rows + 4;

@@ -708,14 +708,17 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 // streamed and accumulated into acc[r] (RM * NB accumulator sets stay in
 // registers).  Each chunk is thereby staged once per pass instead of once per
 // round.  Rounds past the wave's last block re-read that block (recently
-// fetched, so an L2 hit) and their results are dropped.  The rounds of a pass
-// are finished (scale, mask, noise, argmax) after its last chunk.
+// fetched, so an L2 hit) and their results are dropped.  With a sampling
+// epilogue each round of a pass is finished (scale, mask, noise, argmax) right
+// after its part of the last chunk, while the loads of the next round are in
+// flight; stored logits are written at the end of the pass.
 // ---------------------------------------------------------------------------
 template <int NB, int EPI, bool MASKED, int RM>
 __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParams p) {
   static_assert(kFastRingChunked == 2, "two sub-blocks per chunk, two register buffers");
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block indices and bases stay scalar
   const int l16 = lane & 15, grp = lane >> 4;
   const TileRange tr = tile_range(p);
   const int rs = p.h_rowstride;
@@ -749,15 +752,20 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
   // the wave's last block of the tile (the clamp target of empty rounds)
   const int64_t nown = tr.mb_hi - tr.mb_lo - wave > 0 ? (tr.mb_hi - tr.mb_lo - wave + kWaves - 1) / kWaves : 0;
   const int64_t last_blk = nown > 0 ? tr.mb_lo + (nown - 1) * kWaves + wave : tr.mb_hi - 1;
-  auto row_ptr = [&](int pass, int r) {
-    int64_t mb = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
-    mb = mb < tr.mb_hi ? mb : last_blk;
-    return w_row(p, tr, mb, l16) + grp * 64;
+  // W addressing: a scalar base per 16-row block plus one 32-bit lane offset
+  // (row l16, clamped to the tile's last row, and the lane group's 128 bytes)
+  const int64_t tile_end = tr.mb_hi * 16 < p.V ? tr.mb_hi * 16 : p.V;
+  const uint32_t ldw2 = (uint32_t)p.ldw * 2u;
+  auto blk = [&](int pass, int r) {
+    const int64_t mb = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
+    return mb < tr.mb_hi ? mb : last_blk;
   };
-  auto load = [&](u32x4_t (&buf)[8], const uint16_t* row, int sb) {
-    const u32x4_t* src = (const u32x4_t*)(row + sb * 256);
+  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) {
+    const char* base = (const char*)(p.W + mb * 16 * p.ldw) + sb * 512;
+    const int lim = (int)(tile_end - mb * 16);
+    const uint32_t off = (uint32_t)(l16 < lim ? l16 : lim - 1) * ldw2 + (uint32_t)grp * 128u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) buf[e] = src[e];
+    for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(base + off + e * 16);
   };
   auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hb, f32x4_t (&a)[NB]) {
     u32x4_t h0[NB], h1[NB];
@@ -786,7 +794,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
   auto finish = [&](int pass, int r, const f32x4_t (&a)[NB]) {
     const int64_t mbg = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
     if (mbg >= tr.mb_hi) return;
-    const int64_t v0 = mbg * 16 + grp * 4;
+    const int v0 = (int)(mbg * 16) + grp * 4;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int b = nb * 16 + l16;
@@ -817,14 +825,16 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
       *(u32x4_t*)(smem + bufbytes + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
     }
     h_chunk_dma(p, 0, smem);
-    __builtin_amdgcn_s_waitcnt(0);  // the LDS copies of this wave have landed
-    __syncthreads();
-
-    const uint16_t* rowp[RM];
+    int64_t rowp[RM];  // the wave's block in each round of the pass
 #pragma unroll
-    for (int r = 0; r < RM; ++r) rowp[r] = row_ptr(0, r);
+    for (int r = 0; r < RM; ++r) rowp[r] = blk(0, r);
     u32x4_t buf[2][8];
     load(buf[0], rowp[0], 0);
+    // the first W item is in flight behind the chunk-0 copies: once at most its
+    // 8 loads remain (vmcnt 8), this wave's copies have landed
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xF78);
+    __syncthreads();
     int cc = 0;  // chunks consumed
     for (int pass = 0; pass < npass; ++pass) {
       // Waves own RM or RM - 1 blocks in a pass (tiles differ by at most one
@@ -838,7 +848,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
         const int nc = c + 1 < nchunk ? c + 1 : 0;  // the chunk staged next
         const bool last_c = c + 1 == nchunk;
         const int np = last_c && pass + 1 < npass ? pass + 1 : pass;
-        const uint16_t* next_row = last_c ? row_ptr(np, 0) : rowp[0];  // first item of the next chunk
+        const int64_t next_row = last_c ? blk(np, 0) : rowp[0];  // first item of the next chunk
         const int next_sb = last_c ? 0 : (c + 1) * 2;
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
@@ -861,6 +871,17 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
             __builtin_amdgcn_sched_barrier(0);
             compute(buf[sb], hb + sb * 512, acc[r]);
           }
+          // after the pass's last chunk, round r is complete: finish it while
+          // the next item's loads are in flight (sampling epilogues; storing
+          // the logits is cheap and is left to the end of the pass, which
+          // keeps more rounds within the register budget)
+          if (EPI != EPI_STORE && last_c) {
+            __builtin_amdgcn_sched_barrier(0);
+            finish(pass, r, acc[r]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         // the chunk's copies were issued before the last W item (8 loads), so
         // at most those 8 loads may still be outstanding: vmcnt(8)
@@ -868,15 +889,17 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
         __syncthreads();
         ++cc;
       }
+      if (EPI == EPI_STORE) {
 #pragma unroll
-      for (int r = 0; r < RM; ++r) {
-        finish(pass, r, acc[r]);
+        for (int r = 0; r < RM; ++r) {
+          finish(pass, r, acc[r]);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
       }
       if (pass + 1 < npass) {
 #pragma unroll
-        for (int r = 0; r < RM; ++r) rowp[r] = row_ptr(pass + 1, r);
+        for (int r = 0; r < RM; ++r) rowp[r] = blk(pass + 1, r);
       }
     }
   }
@@ -1065,14 +1088,23 @@ static hipError_t launch_variant(const StreamParams& p, const StreamConfig& c, h
 template <int EPI, bool MK, int NB>
 static hipError_t launch_kouter(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
   const int g = p.n_tiles, L = c.lds_bytes;
+  constexpr int cap = kouter_max_rounds(EPI, NB, MK);
   switch (c.rm) {
     case 1: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 1>, g, L, s, p);
     case 2: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 2>, g, L, s, p);
-    case 3: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 3>, g, L, s, p);
-    case 4: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 4>, g, L, s, p);
-    case 5: return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 5>, g, L, s, p);
-    default: return hipErrorInvalidValue;
+    case 3:
+      if constexpr (cap >= 3) return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 3>, g, L, s, p);
+      break;
+    case 4:
+      if constexpr (cap >= 4) return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 4>, g, L, s, p);
+      break;
+    case 5:
+      if constexpr (cap >= 5) return launch_with_lds(fmms_kouter_kernel<NB, EPI, MK, 5>, g, L, s, p);
+      break;
+    default:
+      break;
   }
+  return hipErrorInvalidValue;
 }
 
 // The noise table is planned only for the fast driver and the sampling epilogues.
