@@ -311,6 +311,40 @@ __device__ __forceinline__ const uint16_t* w_row(const StreamParams& p, const Ti
   return p.W + row * p.ldw;
 }
 
+// W addressing of the streaming loops: a scalar base per 16-row block plus a
+// 32-bit lane offset (row l16 and the lane group's 128 bytes).  Both lane
+// offsets are computed once: rows of the tile's last block are clamped to the
+// tile's last row (a partial block at the end of the vocabulary).  Keeping the
+// multiply out of the loop matters: the fused 32-bit multiply-add the compiler
+// would otherwise emit per load writes a carry to scalar registers, which
+// stalled the W stream on gfx950.
+struct WLane {
+  uint32_t full, last;
+};
+
+__device__ __forceinline__ WLane w_lane(const StreamParams& p, const TileRange& tr, int l16, int grp) {
+  const int64_t tile_end = tr.mb_hi * 16 < p.V ? tr.mb_hi * 16 : p.V;
+  const int lim = (int)(tile_end - (tr.mb_hi - 1) * 16);  // rows of the last block, 1 .. 16
+  const uint32_t ldw2 = (uint32_t)p.ldw * 2u;
+  WLane w;
+  w.full = (uint32_t)l16 * ldw2 + (uint32_t)grp * 128u;
+  w.last = (uint32_t)(l16 < lim ? l16 : lim - 1) * ldw2 + (uint32_t)grp * 128u;
+  return w;
+}
+
+// The 8 x 16 bytes lane (l16, grp) owns of 256-wide sub-block sb of 16-row
+// block mb (uniform across the wave).  A block past the tile (a wave idle in
+// the tile's last round) reads the tile's last block; its results are
+// discarded.
+__device__ __forceinline__ void w_load8(const StreamParams& p, const TileRange& tr, const WLane& wl, int64_t mb,
+                                        int sb, u32x4_t (&buf)[8]) {
+  mb = mb < tr.mb_hi ? mb : tr.mb_hi - 1;
+  const char* base = (const char*)(p.W + mb * 16 * p.ldw) + sb * 512;
+  const uint32_t off = mb == tr.mb_hi - 1 ? wl.last : wl.full;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(base + off + e * 16);
+}
+
 // ---------------------------------------------------------------------------
 // Streaming drivers.  Both call
 //   body(cur, hbase, sbc, r, t)  -- consume sub-block t (0 .. nsub-1) of round r;
@@ -334,6 +368,8 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
   const int bufbytes = p.h_rows * p.h_rowstride;
   if (tr.rounds == 0) return;
 
+  // per-lane 64-bit row addresses: measured faster here than a scalar block
+  // base plus a lane offset (w_load8), unlike in the chunk-outer kernel
   auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
     const u32x4_t* src = (const u32x4_t*)(w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16) + sb * 256 +
                                           grp * 64);
@@ -752,21 +788,12 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
   // the wave's last block of the tile (the clamp target of empty rounds)
   const int64_t nown = tr.mb_hi - tr.mb_lo - wave > 0 ? (tr.mb_hi - tr.mb_lo - wave + kWaves - 1) / kWaves : 0;
   const int64_t last_blk = nown > 0 ? tr.mb_lo + (nown - 1) * kWaves + wave : tr.mb_hi - 1;
-  // W addressing: a scalar base per 16-row block plus one 32-bit lane offset
-  // (row l16, clamped to the tile's last row, and the lane group's 128 bytes)
-  const int64_t tile_end = tr.mb_hi * 16 < p.V ? tr.mb_hi * 16 : p.V;
-  const uint32_t ldw2 = (uint32_t)p.ldw * 2u;
   auto blk = [&](int pass, int r) {
     const int64_t mb = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
     return mb < tr.mb_hi ? mb : last_blk;
   };
-  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) {
-    const char* base = (const char*)(p.W + mb * 16 * p.ldw) + sb * 512;
-    const int lim = (int)(tile_end - mb * 16);
-    const uint32_t off = (uint32_t)(l16 < lim ? l16 : lim - 1) * ldw2 + (uint32_t)grp * 128u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(base + off + e * 16);
-  };
+  const WLane wl = w_lane(p, tr, l16, grp);
+  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) { w_load8(p, tr, wl, mb, sb, buf); };
   auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hb, f32x4_t (&a)[NB]) {
     u32x4_t h0[NB], h1[NB];
 #pragma unroll
