@@ -337,6 +337,27 @@ def main():
                           "pct_peak": round(100 * ab / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                           "unfused_us_per_step": round(ku_ms * 1e3, 2)})
             log(f"sweep {sweep[-1]}")
+        # several samples per row from one pass over W, against as many single-sample steps
+        for b, S in ((8, 4), (16, 4)):
+            _, Wt = load_W("mid_decode")
+            Ht = H_for("mid_decode", b)
+            outm = torch.empty((b, S), dtype=torch.int32, device=dev)
+            outs = torch.empty(b, dtype=torch.int32, device=dev)
+
+            def ms(i, base):
+                fs.fs_fmms_sample_multi(ctx, Ht, Wt[i % len(Wt)], wt["T"], 0, (base + i) * S, S, out=outm)
+
+            def ss(i, base):
+                fs.fs_fmms_sample(ctx, Ht, Wt[(i // S) % len(Wt)], wt["T"], 0, base + i, out=outs)
+
+            timer.run(lambda i: ms(i, 0), 5)
+            m_ms, _ = timer.run(lambda i: ms(i, 10), max(20, n // 4))
+            timer.run(lambda i: ss(i, 0), 5)
+            s_ms, _ = timer.run(lambda i: ss(i, 10), max(20, n // 4) * S)
+            sweep.append({"workload": "mid_decode_multi", "B": b, "num_samples": S, "d": wt["d"], "V": wt["V"],
+                          "us_per_call": round(m_ms * 1e3, 2), "us_for_same_samples_one_per_call":
+                          round(s_ms * S * 1e3, 2), "speedup": round(s_ms * S / m_ms, 3)})
+            log(f"sweep {sweep[-1]}")
         del weights["mid_decode"]
         torch.cuda.empty_cache()
         # masked workload

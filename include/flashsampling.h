@@ -114,6 +114,19 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
                    const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* tile_max,
                    int32_t* tile_arg, int path);
 
+/* Several samples per row from one pass over W.
+ *   out_idx [B, num_samples] int32 (row-major): out_idx[b * num_samples + s] is
+ *   the id fs_fmms_sample returns for row b at step `step + s` (64-bit
+ *   wrap-around), i.e. num_samples independent draws from the same
+ *   softmax(logits / T) with the noise streams of consecutive steps.  W is
+ *   read once per 64 (row, sample) pairs.  Other arguments as in
+ *   fs_fmms_sample; no top-k or tile maxima here.
+ *   [readus.org summary, code guide item 1: the API takes a number of samples]
+ * Requires num_samples >= 1 and B * num_samples < 2^31. */
+int fs_fmms_sample_multi(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                         int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                         const uint32_t* mask, int64_t ldm, int num_samples, int32_t* out_idx, int path);
+
 /* Unfused comparison path: the same LM-head product written to HBM as fp32
  * logits, then a separate sampling kernel reads them back and applies the
  * same scaling, mask, top-k, noise and argmax.  Same arguments and result as

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     fs_debug_philox,
     fs_destroy,
     fs_fmms_sample,
+    fs_fmms_sample_multi,
     fs_fmms_tiling,
     fs_group_combine,
     fs_group_summary,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "fs_last_error": (ctypes.c_char_p, []),
     "fs_fmms_tiling": (_I, [_P, _I, _I, _I64, _I, ctypes.POINTER(_I64), _P]),
     "fs_fmms_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _P, _I]),
+    "fs_fmms_sample_multi": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _I]),
     "fs_unfused_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _I64,
                                _I]),
     "fs_group_summary": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _F, _U64, _U64, _P, _I64, _P, _I]),
@@ -145,6 +146,24 @@ def fs_fmms_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: floa
     _check(_lib.fs_fmms_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(), _dptr(tile_max),
                                _dptr(tile_arg), path))
+    return out
+
+
+def fs_fmms_sample_multi(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+                         num_samples: int, mask: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                         path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Returns out: [B, num_samples] int32; out[b, s] is the sample of row b at step `step + s`."""
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if out is None:
+        out = torch.empty((B, num_samples), dtype=torch.int32, device=H.device)
+    if out.dtype != torch.int32 or not out.is_contiguous() or out.numel() != B * num_samples:
+        raise TypeError("out must be a contiguous int32 tensor of B * num_samples elements")
+    mptr, ldm = _mask_args(mask)
+    _check(_lib.fs_fmms_sample_multi(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
+                                     float(temperature), seed, step, mptr, ldm, num_samples, out.data_ptr(), path))
     return out
 
 

@@ -167,10 +167,14 @@ void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int
 // kMfmaMaxB rows (each chunk streams W once); with a mask, chunks are also
 // small enough for their tile masks to fit the LDS staging area.  `per_chunk`
 // adjusts the output pointers of a chunk that starts at batch row r0.
+// With base.samples > 1, base.B counts the call's virtual rows (row h, sample
+// s at h * samples + s): H and row_offset stay those of the call and each chunk
+// starts at virtual row r0; `max_rows` bounds a chunk by the context's workspace.
 template <typename F>
-int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk) {
+int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk,
+                      int max_rows = fsk::kMfmaMaxB) {
   const int B = base.B;
-  int chunk = fsk::kMfmaMaxB;
+  int chunk = fsk::kMfmaMaxB < max_rows ? fsk::kMfmaMaxB : max_rows;
   if (base.mask) {
     const int64_t rows = fsk::kMaskLdsMax / (4 * fsk::tile_mask_words(base.n_mblocks, base.n_tiles));
     if (rows < 1) return fail(FS_ERR_UNSUPPORTED, "V=%lld: a tile's mask does not fit the LDS staging area", (long long)base.V);
@@ -180,8 +184,12 @@ int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t str
     const int Bc = (B - r0) < chunk ? (B - r0) : chunk;
     fsk::StreamParams p = base;
     p.B = Bc;
-    p.H = base.H + (int64_t)r0 * base.ldh;
-    p.row_offset = r0;
+    if (base.samples > 1) {
+      p.vrow0 = r0;
+    } else {
+      p.H = base.H + (int64_t)r0 * base.ldh;
+      p.row_offset = r0;
+    }
     per_chunk(p, r0);
     fsk::StreamConfig cfg;
     int rc = choose_config(Bc, path, cfg);
@@ -386,6 +394,26 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
     c.dbg_max = tile_max ? tile_max + (int64_t)r0 * nt : nullptr;
     c.dbg_arg = tile_arg ? tile_arg + (int64_t)r0 * nt : nullptr;
   });
+}
+
+int fs_fmms_sample_multi(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                         int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                         const uint32_t* mask, int64_t ldm, int num_samples, int32_t* out_idx, int path) {
+  int rc = check_operands(ctx, H, ldh, W, ldw, B, d, V, temperature, mask, ldm, V);
+  if (rc != FS_OK) return rc;
+  if (!out_idx) return fail(FS_ERR_INVALID_ARG, "out_idx is NULL");
+  if (num_samples < 1) return fail(FS_ERR_INVALID_ARG, "num_samples=%d must be >= 1", num_samples);
+  if ((int64_t)B * num_samples > INT32_MAX)
+    return fail(FS_ERR_INVALID_ARG, "B * num_samples = %lld exceeds 2^31 - 1", (long long)B * num_samples);
+  if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  fsk::StreamParams p;
+  fill_common(p, ctx, H, ldh, W, ldw, B * num_samples, d, V, temperature, seed, step, mask, ldm);
+  p.samples = num_samples;
+  return run_stream_chunks(
+      p, path, fsk::EPI_FLAT, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) { c.out_idx = out_idx + r0; },
+      ctx->max_B);
 }
 
 int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,

@@ -25,6 +25,12 @@ struct StreamParams {
   int64_t V;             // rows of W in this launch
   int64_t vocab_offset;  // global vocab id of W row 0 (noise and mask use global ids)
   int row_offset;        // global batch row of H row 0 (noise counter and mask row)
+  // Several samples per row: batch row b of the launch is virtual row
+  // r = vrow0 + b = h * samples + s of the call, drawing sample s of H row h
+  // with noise at step + s (H then points at the call's first row).  With
+  // samples == 1, batch row b is H row b.
+  int samples;
+  int vrow0;
   float inv_t;
   uint32_t seed_lo, seed_hi, step_lo, step_hi;
   const uint32_t* mask;  // [B, ldm] words or null

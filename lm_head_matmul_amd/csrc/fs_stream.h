@@ -121,6 +121,30 @@ __device__ __forceinline__ TileRange tile_range(const StreamParams& p) {
   return t;
 }
 
+// H row, noise row and noise step of batch row b of a launch (see
+// StreamParams::samples).
+struct VRow {
+  int h;
+  uint32_t row, step_lo, step_hi;
+};
+
+__device__ __forceinline__ VRow vrow_of(const StreamParams& p, int b) {
+  VRow v;
+  v.step_lo = p.step_lo;
+  v.step_hi = p.step_hi;
+  if (p.samples <= 1) {
+    v.h = b;
+  } else {
+    const int r = p.vrow0 + b;
+    v.h = r / p.samples;
+    const uint32_t smp = (uint32_t)(r - v.h * p.samples);
+    v.step_lo = p.step_lo + smp;
+    v.step_hi = p.step_hi + (v.step_lo < smp ? 1u : 0u);
+  }
+  v.row = (uint32_t)(p.row_offset + v.h);
+  return v;
+}
+
 // H chunk `cidx` (k in [cidx*cs*256, ...)) as 16-byte pieces: piece P = n * (cs*32) + q.
 // The load is unconditional (row and k clamped into H); h_valid says whether
 // the piece lies inside H (pieces outside are stored as zero).
@@ -131,7 +155,7 @@ __device__ __forceinline__ u32x4_t h_load(const StreamParams& p, int cidx, int P
   const int k = cidx * p.cs * 256 + q * 8;
   const int nc = n < p.B ? n : p.B - 1;
   const int kc = k < p.d ? k : p.d - 8;
-  return *(const u32x4_t*)(p.H + (int64_t)nc * p.ldh + kc);
+  return *(const u32x4_t*)(p.H + (int64_t)vrow_of(p, nc).h * p.ldh + kc);
 }
 
 __device__ __forceinline__ bool h_valid(const StreamParams& p, int cidx, int P) {
@@ -200,7 +224,7 @@ __device__ __forceinline__ void h_chunk_dma(const StreamParams& p, int cidx, uns
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint16_t* src = p.H + cidx * 512 + lane * 8;
   for (int b = wave; b < p.B; b += kWaves)
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)b * p.ldh),
+    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)vrow_of(p, b).h * p.ldh),
                                      (__attribute__((address_space(3))) void*)(buf + b * p.h_rowstride), 16, 0, 0);
 }
 
@@ -227,7 +251,7 @@ __device__ void mask_stage(const StreamParams& p, const TileRange& tr, uint32_t*
       const int b = ii / p.mask_words;
       int64_t w = w_lo + (ii - b * p.mask_words);
       w = w <= w_max ? w : w_max;
-      w4[j] = p.mask[((int64_t)p.row_offset + b) * p.ldm + w];
+      w4[j] = p.mask[(int64_t)vrow_of(p, b).row * p.ldm + w];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -256,9 +280,10 @@ __device__ __forceinline__ uint32_t mask_bits4(const StreamParams& p, const uint
 // order of a lane is increasing in v, so a strict comparison keeps the lowest
 // id on ties.
 // Gumbel noise of the four consecutive vocab ids gv0 .. gv0+3 (gv0 % 4 == 0,
-// global ids) of global batch row `row`: one Philox call.
-__device__ __forceinline__ f32x4_t noise_quad(const StreamParams& p, int gv0, uint32_t row) {
-  const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)gv0 >> 2, row, p.step_lo, p.step_hi);
+// global ids) of batch row b of the launch: one Philox call.
+__device__ __forceinline__ f32x4_t noise_quad(const StreamParams& p, int gv0, int b) {
+  const VRow v = vrow_of(p, b);
+  const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)gv0 >> 2, v.row, v.step_lo, v.step_hi);
   return f32x4_t{gumbel_from_bits(r.w[0]), gumbel_from_bits(r.w[1]), gumbel_from_bits(r.w[2]),
                  gumbel_from_bits(r.w[3])};
 }
@@ -273,7 +298,7 @@ __device__ void noise_stage(const StreamParams& p, const TileRange& tr, float* l
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int b = i / quads;
     const int q = i - b * quads;
-    *(f32x4_t*)(lds + b * p.noise_pitch + q * 4) = noise_quad(p, v_base + q * 4, (uint32_t)(p.row_offset + b));
+    *(f32x4_t*)(lds + b * p.noise_pitch + q * 4) = noise_quad(p, v_base + q * 4, b);
   }
 }
 
@@ -606,7 +631,6 @@ template <int NB, int EPI, bool RESIDENT, bool FAST, bool MASKED, bool NOISE_LDS
           int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int Bp = NB * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const TileRange tr = tile_range(p);
@@ -691,7 +715,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
       if (NOISE_LDS)
         g = *(const f32x4_t*)(noise_lds + b * p.noise_pitch + (int)(v0 - tr.mb_lo * 16));
       else
-        g = noise_quad(p, (int)(p.vocab_offset + v0), (uint32_t)(p.row_offset + b));
+        g = noise_quad(p, (int)(p.vocab_offset + v0), b);
       epilogue_quad<EPI>(p, (int)v0, a4, g, bits, bv[nb], bi[nb], lm[nb], ls[nb]);
     }
   };
@@ -837,7 +861,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
       } else {
         const float a4[4] = {a[nb][0], a[nb][1], a[nb][2], a[nb][3]};
         const uint32_t bits = mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
-        const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), (uint32_t)(p.row_offset + b));
+        const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), b);
         epilogue_quad<EPI>(p, (int)v0, a4, g, bits, bv[nb], bi[nb], lm[nb], ls[nb]);
       }
       __builtin_amdgcn_sched_barrier(0);  // one N-block's noise at a time (register pressure)
@@ -1015,8 +1039,8 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
       if (v < p.V) p.logits[(int64_t)b * p.ldl + v] = xv;
       return;
     }
-    const int64_t grow = (int64_t)p.row_offset + b;
-    const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)(gv >> 2), (uint32_t)grow, p.step_lo, p.step_hi);
+    const VRow vr = vrow_of(p, b);
+    const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)(gv >> 2), vr.row, vr.step_lo, vr.step_hi);
     const uint32_t q = (uint32_t)(gv & 3);
     const uint32_t word = q == 0 ? r.w[0] : q == 1 ? r.w[1] : q == 2 ? r.w[2] : r.w[3];
     const bool ok = v < p.V && ((mask_bits4<MASKED>(p, mask_lds, mw_lo, gv & ~(int64_t)3, b) >> q) & 1u);

@@ -20,16 +20,20 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from lm_head_matmul_amd import build
+        # the build script by path: importing the package would load the library
+        import importlib.util
 
-        build.build()
+        spec = importlib.util.spec_from_file_location("_fs_lib_build", os.path.join(ROOT, "lm_head_matmul_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return ctypes.CDLL(LIB)
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ["fs_create", "fs_destroy", "fs_last_error", "fs_fmms_tiling", "fs_fmms_sample",
-                     "fs_unfused_sample", "fs_group_summary", "fs_group_combine", "fs_debug_philox",
+                     "fs_fmms_sample_multi", "fs_unfused_sample", "fs_group_summary", "fs_group_combine", "fs_debug_philox",
                      "fs_debug_gumbel_bits", "fs_debug_gumbel_scan"]:
         assert required in names
 
@@ -52,6 +56,8 @@ def test_null_context_is_rejected(lib):
     rc = L.fs_fmms_sample(None, None, None, 0, None, 0, 1, 8, 16, 1.0, 0, 0, None, 0, 0, None, None, None, 0)
     assert rc == binding.FS_ERR_INVALID_ARG
     assert b"ctx" in L.fs_last_error()
+    assert L.fs_fmms_sample_multi(None, None, None, 0, None, 0, 1, 8, 16, 1.0, 0, 0, None, 0, 2, None, 0) == \
+        binding.FS_ERR_INVALID_ARG
     assert L.fs_group_combine(None, None, None, 1, 1, 0, 0, 0, None) == binding.FS_ERR_INVALID_ARG
     assert L.fs_debug_gumbel_scan(None, None, None) == binding.FS_ERR_INVALID_ARG
 
