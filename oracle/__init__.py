@@ -52,6 +52,10 @@ def lib():
             "fso_grouped_sample_steps": (None, [P, i32, i64, f32, u64, u64, i64, P, i64, P, i32, i32, P]),
             "fso_fmms_sample": (None, [P, i64, P, i64, i32, i32, i64, f32, u64, u64, P, i64, i32, P]),
             "fso_num_threads": (i32, []),
+            "fso_uniform_bits": (u32, [u64, u64, u32]),
+            "fso_uniform64": (ctypes.c_double, [u32]),
+            "fso_cdf_sample_row": (i64, [P, i64, f32, P, ctypes.c_double]),
+            "fso_cdf_sample_rows_steps": (None, [P, P, i32, i64, f32, u64, u64, i32, P, i64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -182,6 +186,34 @@ def sample_steps(L, T, seed, step0, nsteps, mask=None, top_k=0):
     out = np.empty((nsteps, B), np.int32)
     lib().fso_sample_steps(_ptr(L), B, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, _ptr(out))
     return out
+
+
+def uniform_bits(seed: int, step: int, row: int) -> int:
+    return int(lib().fso_uniform_bits(seed, step, row))
+
+
+def uniform64(r: int) -> float:
+    return float(lib().fso_uniform64(r))
+
+
+def cdf_sample_row(logit_row, T, u, mask_row=None) -> int:
+    x = _c(logit_row, np.float32)
+    m = None if mask_row is None else _c(mask_row, np.uint32)
+    return int(lib().fso_cdf_sample_row(_ptr(x), x.shape[0], T, _ptr(m), u))
+
+
+def cdf_sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None):
+    """Conventional comparator: (ids, u), each [nsteps, R]."""
+    L = _c(L, np.float32)
+    R, V = L.shape
+    rows = _c(rows, np.int32)
+    m = None if mask is None else _c(mask, np.uint32)
+    ldm = 0 if m is None else m.shape[1]
+    ids = np.empty((nsteps, R), np.int32)
+    u = np.empty((nsteps, R), np.float64)
+    lib().fso_cdf_sample_rows_steps(_ptr(L), _ptr(rows), R, V, T, seed, step0, nsteps, _ptr(m), ldm, _ptr(ids),
+                                    _ptr(u))
+    return ids, u
 
 
 def sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None, top_k=0):

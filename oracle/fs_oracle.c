@@ -51,6 +51,10 @@
  *       range the vocabulary never reaches; k* = argmax_k (lse_k + g'_k), the
  *       sample is that group's own argmax.  Mode M: k* = argmax_k pmax_k,
  *       which reproduces the flat argmax exactly.
+ *   R9  conventional comparator (not the method): one uniform per row and step
+ *       from word 0 of Philox(key = seed, counter = (0x80000000, row, step)),
+ *       u = (r+1)/(2^32+1); the sample is the first allowed id whose running
+ *       sum of exp(s - max s) exceeds u times the total (fp64).
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared.
  */
@@ -119,6 +123,21 @@ uint32_t fso_group_noise_bits(uint64_t seed, uint64_t step, uint32_t row, uint32
   fso_philox4x32_10(key, ctr, out);
   return out[0];
 }
+
+/* Reading R9: the uniform of the conventional comparator's row `row` is
+ * driven by word 0 of Philox(key = seed, counter = (0x80000000, row, step)),
+ * a counter range that neither the vocabulary (v >> 2 < 2^29) nor the group
+ * noise (0x40000000 | k, k < 2^30) reaches. */
+uint32_t fso_uniform_bits(uint64_t seed, uint64_t step, uint32_t row) {
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t ctr[4] = {0x80000000u, row, (uint32_t)step, (uint32_t)(step >> 32)};
+  uint32_t out[4];
+  fso_philox4x32_10(key, ctr, out);
+  return out[0];
+}
+
+/* u = (r + 1) / (2^32 + 1), strictly inside (0, 1), in fp64. */
+double fso_uniform64(uint32_t r) { return ((double)r + 1.0) / 4294967297.0; }
 
 /* ------------------------------------------------------------------------ */
 /* Standard Gumbel noise from one 32-bit word (reading R3).                  */
@@ -293,6 +312,60 @@ void fso_sample_from_logits(const float* logits, int B, int64_t V, float T, uint
     out_idx[b] = (int32_t)fso_argmax(p, V);
     if (!p_out) free(p);
   }
+}
+
+/* Conventional comparator (not the method): sample one row by inverse CDF.
+ * Scores as R2 and R5 (mask, no top-k); weights w_v = exp(s_v - m) in fp64
+ * over the allowed ids, m their largest score; Z = sum of w; the sample is
+ * the first id whose running sum of w exceeds u * Z (the last allowed id if
+ * rounding leaves the sum at or below it); -1 if no id is allowed.  This is
+ * the softmax, prefix-sum and search pipeline that the fused sampler replaces.
+ * [readus.org FlashSampling summary, the essay part: the softmax pipeline
+ * exponentiates, normalizes and scans a cumulative array to pick a token] */
+int64_t fso_cdf_sample_row(const float* logit_row, int64_t V, float T, const uint32_t* mask_row, double u) {
+  float* s = (float*)malloc((size_t)V * sizeof(float));
+  fso_scores_row(logit_row, V, T, mask_row, 0, s);
+  double m = -INFINITY;
+  int64_t last = -1;
+  for (int64_t v = 0; v < V; ++v)
+    if (s[v] != -INFINITY) {
+      if ((double)s[v] > m) m = (double)s[v];
+      last = v;
+    }
+  int64_t pick = last;
+  if (last >= 0) {
+    double Z = 0.0;
+    for (int64_t v = 0; v < V; ++v)
+      if (s[v] != -INFINITY) Z += exp((double)s[v] - m);
+    const double target = u * Z;
+    double run = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+      if (s[v] == -INFINITY) continue;
+      run += exp((double)s[v] - m);
+      if (run > target) {
+        pick = v;
+        break;
+      }
+    }
+  }
+  free(s);
+  return pick;
+}
+
+/* The comparator over steps step0 .. step0+nsteps-1 of global rows `rows`
+ * (logits[i] belongs to row rows[i]); out is [nsteps, R]; u_out, if not NULL,
+ * receives the uniforms. */
+void fso_cdf_sample_rows_steps(const float* logits, const int32_t* rows, int R, int64_t V, float T, uint64_t seed,
+                               uint64_t step0, int nsteps, const uint32_t* mask, int64_t ldm, int32_t* out,
+                               double* u_out) {
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int t = 0; t < nsteps; ++t)
+    for (int i = 0; i < R; ++i) {
+      const double u = fso_uniform64(fso_uniform_bits(seed, step0 + (uint64_t)t, (uint32_t)rows[i]));
+      if (u_out) u_out[(int64_t)t * R + i] = u;
+      out[(int64_t)t * R + i] = (int32_t)fso_cdf_sample_row(logits + (int64_t)i * V, V, T,
+                                                            mask ? mask + (int64_t)rows[i] * ldm : NULL, u);
+    }
 }
 
 /* Many consecutive steps step0 .. step0+nsteps-1 for fixed logits; out is
