@@ -337,6 +337,30 @@ def main():
                           "pct_peak": round(100 * ab / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                           "unfused_us_per_step": round(ku_ms * 1e3, 2)})
             log(f"sweep {sweep[-1]}")
+        # the conventional comparator (logits, softmax, prefix sum, inverse-CDF search) and the
+        # LM-head GEMM alone through hipBLASLt (torch's linear, bf16 logits), next to the fused sampler
+        for b in (1, 8, 64):
+            _, Wt = load_W("mid_decode")
+            Ht = H_for("mid_decode", b)
+            outc = torch.empty(b, dtype=torch.int32, device=dev)
+            lgc = torch.empty((b, (wt["V"] + 3) // 4 * 4), dtype=torch.float32, device=dev)
+
+            def cs(i, base):
+                fs.fs_softmax_sample(ctx, Ht, Wt[i % len(Wt)], wt["T"], 0, base + i, out=outc, logits_ws=lgc)
+
+            def mm(i, base):
+                torch.nn.functional.linear(Ht, Wt[i % len(Wt)])
+
+            timer.run(lambda i: cs(i, 0), 5)
+            c_ms, _ = timer.run(lambda i: cs(i, 10), max(20, n // 4))
+            timer.run(lambda i: mm(i, 0), 5)
+            g_ms, _ = timer.run(lambda i: mm(i, 10), max(20, n // 4))
+            f_ms, _ = time_fmms("mid_decode", b, max(20, n // 4), 5, wt["T"])
+            sweep.append({"workload": "mid_decode_conventional", "B": b, "d": wt["d"], "V": wt["V"],
+                          "conventional_us_per_step": round(c_ms * 1e3, 2), "fmms_us_per_step": round(f_ms * 1e3, 2),
+                          "torch_linear_gemm_only_us": round(g_ms * 1e3, 2),
+                          "fmms_speedup_vs_conventional": round(c_ms / f_ms, 3)})
+            log(f"sweep {sweep[-1]}")
         # several samples per row from one pass over W, against as many single-sample steps
         for b, S in ((8, 4), (16, 4)):
             _, Wt = load_W("mid_decode")

@@ -138,6 +138,24 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
                       const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* logits_ws,
                       int64_t ldl, int path);
 
+/* Conventional comparator, not the method: the softmax pipeline the fused
+ * sampler replaces.  The LM-head product goes to logits_ws as fp32 logits, a
+ * softmax of s = logit / T over the allowed ids overwrites them in place with
+ * probabilities (masked ids get 0), and an inverse-CDF search draws the sample:
+ * with u = (r + 1) / (2^32 + 1), r = word 0 of Philox4x32-10(key = seed,
+ * counter = (0x80000000, b, lo32 step, hi32 step)), out_idx[b] is the first id
+ * whose running sum of probabilities exceeds u times their total (-1 if the
+ * row has no allowed id).  A draw from the same softmax(logits / T) as
+ * fs_fmms_sample, but not the same draw.
+ *   [readus.org summary, the essay part on the softmax pipeline: exponentiate,
+ *    normalize and scan a cumulative array]
+ * logits_ws: [B, ldl] fp32 device buffer, ldl >= V, ldl % 4 == 0, 16-byte
+ *       aligned; holds the probabilities on return.
+ * Other arguments and requirements as in fs_fmms_sample (no top-k). */
+int fs_softmax_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                      int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                      const uint32_t* mask, int64_t ldm, int32_t* out_idx, float* logits_ws, int64_t ldl, int path);
+
 /* Grouped / online variant: summary of one vocabulary group.
  *   W_group [G, d] bf16 (row stride ldw) holds the LM-head rows of global vocab
  *   ids [vocab_offset, vocab_offset + G); noise uses the global ids, so the

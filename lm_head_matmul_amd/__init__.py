@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     fs_group_combine,
     fs_group_summary,
     fs_last_error,
+    fs_softmax_sample,
     fs_unfused_sample,
     summary_views,
 )

@@ -44,6 +44,7 @@ SIGNATURES = {
     "fs_fmms_sample_multi": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _I]),
     "fs_unfused_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _I64,
                                _I]),
+    "fs_softmax_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _P, _P, _I64, _I]),
     "fs_group_summary": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _F, _U64, _U64, _P, _I64, _P, _I]),
     "fs_group_combine": (_I, [_P, _P, _P, _I, _I, _U64, _U64, _I, _P]),
     "fs_debug_philox": (_I, [_P, _P, _U64, _U64, _I, _I64, _I64, _P, _P]),
@@ -184,6 +185,27 @@ def fs_unfused_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: f
     _check(_lib.fs_unfused_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                   float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(),
                                   logits_ws.data_ptr(), logits_ws.stride(0), path))
+    return out
+
+
+def fs_softmax_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+                      mask: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                      logits_ws: torch.Tensor | None = None, path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Conventional comparator (softmax, prefix sum, inverse CDF); logits_ws holds the probabilities after."""
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=H.device)
+    if logits_ws is None:
+        logits_ws = torch.empty((B, (V + 3) // 4 * 4), dtype=torch.float32, device=H.device)
+    if logits_ws.dtype != torch.float32 or logits_ws.dim() != 2 or logits_ws.stride(1) != 1:
+        raise TypeError("logits_ws must be a 2-D row-major float32 tensor")
+    mptr, ldm = _mask_args(mask)
+    _check(_lib.fs_softmax_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
+                                  float(temperature), seed, step, mptr, ldm, out.data_ptr(), logits_ws.data_ptr(),
+                                  logits_ws.stride(0), path))
     return out
 
 

@@ -37,6 +37,8 @@ struct fs_ctx {
   int32_t* topk_cand_n;
   float* topk_seg_val;
   int32_t* topk_seg_idx;
+  // conventional comparator: [max_B][kCdfMaxSeg] segment max, sum of exp, sum of probabilities
+  float* cdf_ws;
 };
 
 namespace {
@@ -294,11 +296,18 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     delete c;
     return hip_fail(e, "hipMemset(workspace)");
   }
+  e = hipMalloc(&c->cdf_ws, (size_t)3 * max_B * fsk::kCdfMaxSeg * sizeof(float));
+  if (e != hipSuccess) {
+    (void)hipFree(c->base);
+    delete c;
+    return hip_fail(e, "hipMalloc(comparator workspace)");
+  }
   if (max_top_k > 0) {
     c->topk_rows = max_B < fsk::kMfmaMaxB ? max_B : fsk::kMfmaMaxB;
     c->topk_ldl = (max_V + 3) / 4 * 4;
     e = hipMalloc(&c->topk_ws, (size_t)c->topk_rows * (size_t)c->topk_ldl * sizeof(float));
     if (e != hipSuccess) {
+      (void)hipFree(c->cdf_ws);
       (void)hipFree(c->base);
       delete c;
       return hip_fail(e, "hipMalloc(top-k workspace)");
@@ -314,6 +323,7 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     if (e != hipSuccess) {
       if (c->topk_sel) (void)hipFree(c->topk_sel);
       (void)hipFree(c->topk_ws);
+      (void)hipFree(c->cdf_ws);
       (void)hipFree(c->base);
       delete c;
       return hip_fail(e, "top-k selection workspace");
@@ -335,6 +345,7 @@ void fs_destroy(fs_ctx* ctx) {
   if (ctx->base) (void)hipFree(ctx->base);
   if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
   if (ctx->topk_sel) (void)hipFree(ctx->topk_sel);
+  if (ctx->cdf_ws) (void)hipFree(ctx->cdf_ws);
   delete ctx;
 }
 
@@ -458,6 +469,55 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   q.out_idx = out_idx;
   hipError_t e = fsk::launch_sample_logits(q, s);
   if (e != hipSuccess) return hip_fail(e, "sampling kernel launch");
+  return FS_OK;
+}
+
+int fs_softmax_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                      int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                      const uint32_t* mask, int64_t ldm, int32_t* out_idx, float* logits_ws, int64_t ldl, int path) {
+  int rc = check_operands(ctx, H, ldh, W, ldw, B, d, V, temperature, mask, ldm, V);
+  if (rc != FS_OK) return rc;
+  if (!out_idx) return fail(FS_ERR_INVALID_ARG, "out_idx is NULL");
+  if (!logits_ws || !aligned16(logits_ws)) return fail(FS_ERR_INVALID_ARG, "logits_ws must be a 16-byte aligned device pointer");
+  if (ldl < V || ldl % 4 != 0) return fail(FS_ERR_INVALID_ARG, "ldl=%lld must be >= V and a multiple of 4", (long long)ldl);
+  if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  hipStream_t s = (hipStream_t)stream;
+  fsk::StreamParams p;
+  fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, nullptr, 0);
+  rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
+    c.logits = logits_ws + (int64_t)r0 * ldl;
+    c.ldl = ldl;
+  });
+  if (rc != FS_OK) return rc;
+  fsk::CdfParams q;
+  std::memset(&q, 0, sizeof q);
+  q.logits = logits_ws;
+  q.ldl = ldl;
+  q.B = B;
+  q.V = (int)V;
+  q.inv_t = 1.0f / temperature;
+  q.seed_lo = (uint32_t)seed;
+  q.seed_hi = (uint32_t)(seed >> 32);
+  q.step_lo = (uint32_t)step;
+  q.step_hi = (uint32_t)(step >> 32);
+  q.mask = mask;
+  q.ldm = ldm;
+  // about 2048 workgroups per launch, segments of at least 512 quads
+  const int64_t nq = (V + 3) / 4;
+  int64_t seg = 2048 / B;
+  if (seg > nq / 512) seg = nq / 512;
+  if (seg > fsk::kCdfMaxSeg) seg = fsk::kCdfMaxSeg;
+  if (seg < 1) seg = 1;
+  q.n_seg = (int)seg;
+  const size_t plane = (size_t)ctx->max_B * fsk::kCdfMaxSeg;
+  q.seg_m = ctx->cdf_ws;
+  q.seg_z = ctx->cdf_ws + plane;
+  q.seg_p = ctx->cdf_ws + 2 * plane;
+  q.out_idx = out_idx;
+  hipError_t e = fsk::launch_cdf_sample(q, s);
+  if (e != hipSuccess) return hip_fail(e, "comparator sampling launch");
   return FS_OK;
 }
 

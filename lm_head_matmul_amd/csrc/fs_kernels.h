@@ -99,6 +99,24 @@ struct TopkParams {
   int32_t* seg_idx;
 };
 
+// Conventional comparator (softmax, prefix sum, inverse-CDF search) over
+// stored fp32 logits, overwritten in place by the probabilities.
+struct CdfParams {
+  float* logits;  // [B][ldl]: logits in, probabilities out
+  int64_t ldl;
+  int B;
+  int V;
+  float inv_t;
+  uint32_t seed_lo, seed_hi, step_lo, step_hi;
+  const uint32_t* mask;  // [B, ldm] words or null
+  int64_t ldm;
+  int n_seg;       // segments per row (<= kCdfMaxSeg)
+  float* seg_m;    // [B][kCdfMaxSeg] segment max of s
+  float* seg_z;    // [B][kCdfMaxSeg] segment sum of exp(s - segment max)
+  float* seg_p;    // [B][kCdfMaxSeg] segment sum of the written probabilities
+  int32_t* out_idx;
+};
+
 // Kernel selection for a streaming launch.
 struct StreamConfig {
   bool dot;     // dot-product kernel (else MFMA)
@@ -127,6 +145,7 @@ constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
 constexpr int kTopkBins = 4096;    // first-level bins of the top-k radix select (key bits 31..20)
 constexpr int kTopkCap = 4096;     // boundary-bin ids the segment-parallel selection gathers per row
 constexpr int kTopkMaxSeg = 64;    // segments per row in the top-k launches
+constexpr int kCdfMaxSeg = 64;     // segments per row in the comparator's launches
 
 // Mask words per row staged for the largest tile of a launch.
 inline int64_t tile_mask_words(int64_t n_mblocks, int n_tiles) {
@@ -142,6 +161,7 @@ template <int EPI>
 hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& cfg, hipStream_t stream);
 hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream);
 hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream);
+hipError_t launch_cdf_sample(const CdfParams& p, hipStream_t stream);
 hipError_t launch_group_combine(const GroupSummary* s, int n_groups, int B, uint64_t seed, uint64_t step, int mode,
                                 int32_t* out_idx, hipStream_t stream);
 hipError_t launch_debug_philox(uint64_t seed, uint64_t step, uint32_t row, int64_t v0, int64_t n, uint32_t* r_out,

@@ -428,6 +428,182 @@ __global__ void __launch_bounds__(kThreads) topk_finish_kernel(const TopkParams 
 }
 
 // ---------------------------------------------------------------------------
+// Conventional comparator, not the method: the softmax pipeline the fused
+// sampler replaces [readus.org FlashSampling summary, the essay part: the
+// softmax pipeline exponentiates every score, normalizes, and scans the
+// cumulative array to pick a token].  Over stored logits, three launches:
+//   1. stats (segment, row): segment max and sum of exp(s - max), allowed ids;
+//   2. probs (segment, row): the row's max and total from the segment stats;
+//      p = exp(s - m) / Z written over the logits (0 for masked ids), and the
+//      segment's sum of the written p;
+//   3. search (row): one uniform u per row and step, from word 0 of Philox at
+//      counter (0x80000000, row, step); the segment where the running sum of
+//      segment sums passes u * total; inside it, block-wide scans find the
+//      first id whose running sum passes the remainder.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void cdf_segment(const CdfParams& p, int seg, int64_t& q_lo, int64_t& q_hi) {
+  const int64_t nq = (p.V + 3) / 4;
+  q_lo = (int64_t)seg * nq / p.n_seg;
+  q_hi = (int64_t)(seg + 1) * nq / p.n_seg;
+}
+
+// Allowed-id bits of quad q (ids 4q .. 4q+3) of row b.
+__device__ __forceinline__ uint32_t cdf_bits(const CdfParams& p, int b, int64_t q) {
+  const int v0 = (int)(q * 4);
+  uint32_t bits = p.mask ? (p.mask[(int64_t)b * p.ldm + (v0 >> 5)] >> (uint32_t)(v0 & 31)) & 0xFu : 0xFu;
+  const int left = p.V - v0;
+  if (left < 4) bits &= (1u << left) - 1u;
+  return bits;
+}
+
+// Block-wide merge of (m, z) states; the result is valid in every thread.
+__device__ __forceinline__ void cdf_block_lse(float& m, float& z, float* sm, float* sz) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float om = __shfl_xor(m, off), oz = __shfl_xor(z, off);
+    lse_merge(m, z, om, oz);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    sm[wave] = m;
+    sz[wave] = z;
+  }
+  __syncthreads();
+  m = -INFINITY;
+  z = 0.0f;
+  for (int w = 0; w < kWaves; ++w) lse_merge(m, z, sm[w], sz[w]);
+}
+
+__global__ void __launch_bounds__(kThreads) cdf_stats_kernel(const CdfParams p) {
+  __shared__ float sm[kWaves], sz[kWaves];
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const float* row = p.logits + (int64_t)b * p.ldl;
+  int64_t q_lo, q_hi;
+  cdf_segment(p, seg, q_lo, q_hi);
+  float m = -INFINITY, z = 0.0f;
+  for (int64_t q = q_lo + threadIdx.x; q < q_hi; q += kThreads) {
+    const f32x4_t x = *(const f32x4_t*)(row + q * 4);  // rows are padded to whole quads
+    const uint32_t bits = cdf_bits(p, b, q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((bits >> i) & 1u) lse_push(m, z, x[i] * p.inv_t);
+  }
+  cdf_block_lse(m, z, sm, sz);
+  if (threadIdx.x == 0) {
+    p.seg_m[(int64_t)b * kCdfMaxSeg + seg] = m;
+    p.seg_z[(int64_t)b * kCdfMaxSeg + seg] = z;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) cdf_probs_kernel(const CdfParams p) {
+  __shared__ float sm[kWaves], sz[kWaves];
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float m = -INFINITY, z = 0.0f;
+  for (int i = threadIdx.x; i < p.n_seg; i += kThreads)
+    lse_merge(m, z, p.seg_m[(int64_t)b * kCdfMaxSeg + i], p.seg_z[(int64_t)b * kCdfMaxSeg + i]);
+  cdf_block_lse(m, z, sm, sz);
+  const float inv_z = z > 0.0f ? 1.0f / z : 0.0f;
+  float* row = p.logits + (int64_t)b * p.ldl;
+  int64_t q_lo, q_hi;
+  cdf_segment(p, seg, q_lo, q_hi);
+  float acc = 0.0f;
+  for (int64_t q = q_lo + threadIdx.x; q < q_hi; q += kThreads) {
+    f32x4_t x = *(const f32x4_t*)(row + q * 4);
+    const uint32_t bits = cdf_bits(p, b, q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = ((bits >> i) & 1u) ? __expf(x[i] * p.inv_t - m) * inv_z : 0.0f;
+      acc += x[i];
+    }
+    *(f32x4_t*)(row + q * 4) = x;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  __syncthreads();
+  if (lane == 0) sm[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+    for (int w = 0; w < kWaves; ++w) t += sm[w];
+    p.seg_p[(int64_t)b * kCdfMaxSeg + seg] = t;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) cdf_search_kernel(const CdfParams p) {
+  __shared__ float s_wave[kWaves];
+  __shared__ int s_seg, s_pick, s_last;
+  __shared__ float s_rem;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* row = p.logits + (int64_t)b * p.ldl;
+  if (threadIdx.x == 0) {
+    s_pick = INT32_MAX;
+    s_last = -1;
+  }
+  if (wave == 0) {  // running sum over segments (n_seg <= 64: one lane each)
+    const float ps = lane < p.n_seg ? p.seg_p[(int64_t)b * kCdfMaxSeg + lane] : 0.0f;
+    float incl = ps;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const float total = __shfl(incl, 63);
+    const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, 0x80000000u, (uint32_t)b, p.step_lo, p.step_hi);
+    const float u = (float)(((double)r.w[0] + 1.0) / 4294967297.0);
+    const float target = u * total;
+    // the first segment with mass whose running sum passes the target; if
+    // rounding leaves the running sum at the total, the last one with mass;
+    // none (-1) if the row has no allowed id
+    const uint64_t pass = __ballot(incl > target && ps > 0.0f);
+    const uint64_t pos = __ballot(ps > 0.0f);
+    const int j = pos == 0 ? -1 : (pass != 0 ? __builtin_ctzll(pass) : 63 - __builtin_clzll(pos));
+    const float excl = j > 0 ? __shfl(incl, j - 1) : 0.0f;
+    if (lane == 0) {
+      s_seg = j;
+      s_rem = target - excl;
+    }
+  }
+  __syncthreads();
+  const int j = s_seg;
+  if (j < 0) {
+    if (threadIdx.x == 0) p.out_idx[b] = -1;
+    return;
+  }
+  const float rem = s_rem;
+  int64_t q_lo, q_hi;
+  cdf_segment(p, j, q_lo, q_hi);
+  const int v_lo = (int)(q_lo * 4);
+  const int v_hi = (int)(q_hi * 4 < p.V ? q_hi * 4 : p.V);
+  float base = 0.0f;  // running sum before the current block of kThreads ids
+  for (int v0 = v_lo; v0 < v_hi; v0 += kThreads) {
+    const int v = v0 + threadIdx.x;
+    const float x = v < v_hi ? row[v] : 0.0f;
+    float incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    float before = base;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    if (x > 0.0f) {
+      if (before + incl > rem) atomicMin(&s_pick, v);
+      atomicMax(&s_last, v);
+    }
+    for (int w = 0; w < kWaves; ++w) base += s_wave[w];
+    __syncthreads();
+    if (s_pick != INT32_MAX) break;  // uniform: read after the barrier
+  }
+  if (threadIdx.x == 0) p.out_idx[b] = s_pick != INT32_MAX ? s_pick : s_last;
+}
+
+// ---------------------------------------------------------------------------
 // Grouped combine: one thread per row.
 // ---------------------------------------------------------------------------
 __global__ void group_combine_kernel(const GroupSummary* __restrict__ s, int n_groups, int B, uint32_t seed_lo,
@@ -655,6 +831,14 @@ hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cdf_sample(const CdfParams& p, hipStream_t stream) {
+  const dim3 grid(p.n_seg, p.B);
+  hipLaunchKernelGGL(cdf_stats_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(cdf_probs_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(cdf_search_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
