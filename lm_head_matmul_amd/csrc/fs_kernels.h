@@ -135,6 +135,18 @@ constexpr int kDotMaxB = 2;
 constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
 constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
+// Which 16 bytes of a row's 512-byte sub-block lane group g (0..3) loads with
+// its load instruction e (0..7), and so which 8-value k chunk it feeds to MFMA
+// step e (H is read with the same map): lane_base(g) + e * lane_step bytes.
+//   0: each group a 128-byte run             (128 g + 16 e)
+//   1: the four groups side by side          (16 g + 64 e)
+//   2: two pairs side by side, one per half  (256 (g >> 1) + 16 (g & 1) + 32 e)
+// One load instruction of a wave touches 64, 16 or 32 cache lines.  The map
+// per kernel family is the measured best on gfx950.
+constexpr int kLayoutTable = 0;     // round-major kernel with the tile's noise table in LDS
+constexpr int kLayoutEpilogue = 1;  // round-major kernel, noise in the epilogue (and stored logits)
+constexpr int kLayoutKouter = 1;    // chunk-outer kernel
+constexpr int kLayoutDot = 0;       // dot-product kernel
 // Rounds per pass of the chunk-outer kernel (accumulator sets a wave keeps in
 // registers): the most that fit 256 VGPRs without spilling, by epilogue, batch
 // blocks and masking.

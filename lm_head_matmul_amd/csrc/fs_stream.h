@@ -336,6 +336,15 @@ __device__ __forceinline__ const uint16_t* w_row(const StreamParams& p, const Ti
   return p.W + row * p.ldw;
 }
 
+template <int LAYOUT>
+__device__ __forceinline__ int lane_base(int g) {
+  return LAYOUT == 0 ? g * 128 : LAYOUT == 1 ? g * 16 : (g >> 1) * 256 + (g & 1) * 16;
+}
+template <int LAYOUT>
+constexpr int lane_step() {
+  return LAYOUT == 0 ? 16 : LAYOUT == 1 ? 64 : 32;
+}
+
 // W addressing of the streaming loops: a scalar base per 16-row block plus a
 // 32-bit lane offset (row l16 and the lane group's 128 bytes).  Both lane
 // offsets are computed once: rows of the tile's last block are clamped to the
@@ -347,13 +356,14 @@ struct WLane {
   uint32_t full, last;
 };
 
+template <int LAYOUT>
 __device__ __forceinline__ WLane w_lane(const StreamParams& p, const TileRange& tr, int l16, int grp) {
   const int64_t tile_end = tr.mb_hi * 16 < p.V ? tr.mb_hi * 16 : p.V;
   const int lim = (int)(tile_end - (tr.mb_hi - 1) * 16);  // rows of the last block, 1 .. 16
   const uint32_t ldw2 = (uint32_t)p.ldw * 2u;
   WLane w;
-  w.full = (uint32_t)l16 * ldw2 + (uint32_t)grp * 128u;
-  w.last = (uint32_t)(l16 < lim ? l16 : lim - 1) * ldw2 + (uint32_t)grp * 128u;
+  w.full = (uint32_t)l16 * ldw2 + (uint32_t)lane_base<LAYOUT>(grp);
+  w.last = (uint32_t)(l16 < lim ? l16 : lim - 1) * ldw2 + (uint32_t)lane_base<LAYOUT>(grp);
   return w;
 }
 
@@ -361,13 +371,14 @@ __device__ __forceinline__ WLane w_lane(const StreamParams& p, const TileRange& 
 // block mb (uniform across the wave).  A block past the tile (a wave idle in
 // the tile's last round) reads the tile's last block; its results are
 // discarded.
+template <int LAYOUT>
 __device__ __forceinline__ void w_load8(const StreamParams& p, const TileRange& tr, const WLane& wl, int64_t mb,
                                         int sb, u32x4_t (&buf)[8]) {
   mb = mb < tr.mb_hi ? mb : tr.mb_hi - 1;
   const char* base = (const char*)(p.W + mb * 16 * p.ldw) + sb * 512;
   const uint32_t off = mb == tr.mb_hi - 1 ? wl.last : wl.full;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(base + off + e * 16);
+  for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(base + off + e * lane_step<LAYOUT>());
 }
 
 // ---------------------------------------------------------------------------
@@ -384,7 +395,7 @@ __device__ __forceinline__ void w_load8(const StreamParams& p, const TileRange& 
 // next round).  The loop body has no data-dependent branches, so the
 // compiler's wait counters stay exact and no prefetch is ever drained.
 // ---------------------------------------------------------------------------
-template <int U, bool RESIDENT, class Body, class RoundEnd>
+template <int U, bool RESIDENT, int LAYOUT, class Body, class RoundEnd>
 __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const TileRange& tr, unsigned char* smem,
                                                    Body&& body, RoundEnd&& round_end) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -396,10 +407,10 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
   // per-lane 64-bit row addresses: measured faster here than a scalar block
   // base plus a lane offset (w_load8), unlike in the chunk-outer kernel
   auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
-    const u32x4_t* src = (const u32x4_t*)(w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16) + sb * 256 +
-                                          grp * 64);
+    const char* src = (const char*)(w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16) + sb * 256) +
+                      lane_base<LAYOUT>(grp);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) buf[e] = src[e];
+    for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(src + e * lane_step<LAYOUT>());
   };
   int lr = 0, lsb = 0;  // next position to load; stays on the last sub-block past the end
   auto advance = [&]() {
@@ -469,7 +480,7 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
 // General driver: any d (k tail clamped into the row's last chunk, which meets
 // zeros in the staged H), any chunking, two register buffers.  Conditions are
 // evaluated per sub-block.
-template <bool RESIDENT, class Body, class RoundEnd>
+template <bool RESIDENT, int LAYOUT, class Body, class RoundEnd>
 __device__ __forceinline__ void stream_driver_general(const StreamParams& p, const TileRange& tr, unsigned char* smem,
                                                       Body&& body, RoundEnd&& round_end) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -484,7 +495,7 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
     const uint16_t* base = w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int k = sb * 256 + grp * 64 + e * 8;
+      const int k = sb * 256 + (lane_base<LAYOUT>(grp) + e * lane_step<LAYOUT>()) / 2;
       buf[e] = *(const u32x4_t*)(base + (k < d ? k : d - 8));
     }
   };
@@ -562,13 +573,13 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
   }
 }
 
-template <bool FAST, bool RESIDENT, int RING, class Body, class RoundEnd>
+template <bool FAST, bool RESIDENT, int RING, int LAYOUT, class Body, class RoundEnd>
 __device__ __forceinline__ void stream_driver(const StreamParams& p, const TileRange& tr, unsigned char* smem,
                                               Body&& body, RoundEnd&& round_end) {
   if (FAST)
-    stream_driver_fast<RING, RESIDENT>(p, tr, smem, body, round_end);
+    stream_driver_fast<RING, RESIDENT, LAYOUT>(p, tr, smem, body, round_end);
   else
-    stream_driver_general<RESIDENT>(p, tr, smem, body, round_end);
+    stream_driver_general<RESIDENT, LAYOUT>(p, tr, smem, body, round_end);
 }
 
 // End of an MFMA streaming kernel: reduce each wave's maximizers over its four
@@ -630,6 +641,7 @@ __device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned
 template <int NB, int EPI, bool RESIDENT, bool FAST, bool MASKED, bool NOISE_LDS,
           int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
+  constexpr int LAYOUT = NOISE_LDS ? kLayoutTable : kLayoutEpilogue;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -645,7 +657,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int row = nb * 16 + l16;
-    hoff[nb] = grp * 128 + (row < p.B ? row : p.h_rows - 1) * rs;
+    hoff[nb] = lane_base<LAYOUT>(grp) + (row < p.B ? row : p.h_rows - 1) * rs;
   }
 
   float bv[NB], lm[NB], ls[NB];
@@ -675,7 +687,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 1) * 16);
+      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 1) * lane_step<LAYOUT>());
       __builtin_amdgcn_sched_barrier(0);  // reads of step j + 1 stay ahead of the MFMAs of step j
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -683,7 +695,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
                                                           __builtin_bit_cast(bf16x8_t, h0[nb]), acc[nb], 0, 0, 0);
       if (j + 2 < 8) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 2) * 16);
+        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 2) * lane_step<LAYOUT>());
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -748,7 +760,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING>(p, tr, smem, body, round_end);
+  stream_driver<FAST, RESIDENT, RING, LAYOUT>(p, tr, smem, body, round_end);
   if (kDefer && tr.rounds > 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) finish_nb(tr.rounds - 1, nb);
@@ -775,6 +787,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 // ---------------------------------------------------------------------------
 template <int NB, int EPI, bool MASKED, int RM>
 __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParams p) {
+  constexpr int LAYOUT = kLayoutKouter;
   static_assert(kFastRingChunked == 2, "two sub-blocks per chunk, two register buffers");
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -790,7 +803,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int row = nb * 16 + l16;
-    hoff[nb] = grp * 128 + (row < p.B ? row : p.h_rows - 1) * rs;
+    hoff[nb] = lane_base<LAYOUT>(grp) + (row < p.B ? row : p.h_rows - 1) * rs;
   }
   float bv[NB], lm[NB], ls[NB];
   int32_t bi[NB];
@@ -816,8 +829,8 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
     const int64_t mb = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
     return mb < tr.mb_hi ? mb : last_blk;
   };
-  const WLane wl = w_lane(p, tr, l16, grp);
-  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) { w_load8(p, tr, wl, mb, sb, buf); };
+  const WLane wl = w_lane<LAYOUT>(p, tr, l16, grp);
+  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) { w_load8<LAYOUT>(p, tr, wl, mb, sb, buf); };
   auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hb, f32x4_t (&a)[NB]) {
     u32x4_t h0[NB], h1[NB];
 #pragma unroll
@@ -825,7 +838,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 1) * 16);
+      for (int nb = 0; nb < NB; ++nb) h1[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 1) * lane_step<LAYOUT>());
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -833,7 +846,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
                                                         __builtin_bit_cast(bf16x8_t, h0[nb]), a[nb], 0, 0, 0);
       if (j + 2 < 8) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 2) * 16);
+        for (int nb = 0; nb < NB; ++nb) h0[nb] = *(const u32x4_t*)(hb + hoff[nb] + (j + 2) * lane_step<LAYOUT>());
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1001,20 +1014,20 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
   }
 
   auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc) {
-    const unsigned char* hb = hbase + sbc * 512 + grp * 128;
+    const unsigned char* hb = hbase + sbc * 512 + lane_base<kLayoutDot>(grp);
     u32x4_t h0[BD], h1[BD];
 #pragma unroll
     for (int b = 0; b < BD; ++b) h0[b] = *(const u32x4_t*)(hb + b * rs);
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
 #pragma unroll
-      for (int b = 0; b < BD; ++b) h1[b] = *(const u32x4_t*)(hb + b * rs + (j + 1) * 16);
+      for (int b = 0; b < BD; ++b) h1[b] = *(const u32x4_t*)(hb + b * rs + (j + 1) * lane_step<kLayoutDot>());
       __builtin_amdgcn_sched_barrier(0);  // reads of step j + 1 stay ahead of the products of step j
 #pragma unroll
       for (int b = 0; b < BD; ++b) acc[b] = dot8(cur[j], h0[b], acc[b]);
       if (j + 2 < 8) {
 #pragma unroll
-        for (int b = 0; b < BD; ++b) h0[b] = *(const u32x4_t*)(hb + b * rs + (j + 2) * 16);
+        for (int b = 0; b < BD; ++b) h0[b] = *(const u32x4_t*)(hb + b * rs + (j + 2) * lane_step<kLayoutDot>());
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1065,7 +1078,7 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING>(p, tr, smem, body, round_end);
+  stream_driver<FAST, RESIDENT, RING, kLayoutDot>(p, tr, smem, body, round_end);
   if (tr.rounds > 0) finish_round(tr.rounds - 1);
   if (EPI == EPI_STORE) return;
 
