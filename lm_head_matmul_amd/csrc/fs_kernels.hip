@@ -779,8 +779,11 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   cfg.rm = 0;
   if (!cfg.dot && cfg.fast && p.nchunk > 1) {
     const int64_t rounds = (tile_rows / 16 + kWaves - 1) / kWaves;
+    // passes of equal length: a short last pass would leave waves re-reading
+    // their last block for the rounds they do not own
     const int cap = kouter_max_rounds(epi, cfg.nb, epi != EPI_STORE && p.mask != nullptr);
-    cfg.rm = (int)(rounds < cap ? rounds : cap);
+    const int64_t npass = (rounds + cap - 1) / cap;
+    cfg.rm = (int)((rounds + npass - 1) / npass);
   }
   if (!cfg.dot && cfg.fast && cfg.rm == 0 && epi != EPI_STORE) {
     const int pitch = (int)tile_rows + 4;

@@ -185,3 +185,40 @@ def test_grouped_workload(fs, ctx):
         ref_g = oracle.group_combine(lse, pmax, arg, 0, step, oracle.GROUP_MODE_GUMBEL)
         assert np.mean(ref_g == comb_g.cpu().numpy()) >= 0.999 or np.sum(ref_g != comb_g.cpu().numpy()) <= 1
     say(f"grouped: {steps} steps ok")
+
+
+def test_mid_decode_head_masked_b64(fs, ctx, mid):
+    # four batch blocks with a mask: the chunk-outer kernel's masked form, two passes per tile
+    B = 64
+    mask = synth.bernoulli_mask(B, mid.W.shape[0], 901, 0.3)
+    allowed = synth.unpack_mask(mask, mid.W.shape[0])
+    gpu, _, _, _ = _parity_run(fs, ctx, mid, B, 0.7, 20, mask=mask)
+    for b in range(B):
+        assert np.all(allowed[b, gpu[:, b]]), f"masked id drawn in row {b}"
+
+
+def test_mid_decode_group_summary_b64(fs, ctx, mid):
+    # one large group (131072 ids: several rounds per tile) at four batch blocks
+    import torch
+
+    B, G, T = 64, 131072, 0.7
+    H = synth.workload_H("mid_decode", B=B)
+    Hd = dev_bf16(H)
+    rows = _sample_rows(B)
+    L = oracle.logits(H[rows], mid.W[:G])
+    summ = torch.empty((B, 3), dtype=torch.int32, device="cuda")
+    for step in (0, 1):
+        fs.fs_group_summary(ctx, Hd, mid.Wd[:G], 0, T, 0, step, out=summ)
+        _sync()
+        lse, pmax, arg = (x.cpu().numpy() for x in fs.summary_views(summ))
+        for i, r in enumerate(rows):
+            p = oracle.perturbed_row(L[i], T, 0, step, int(r))
+            s = (L[i] / np.float32(T)).astype(np.float64)
+            m = s.max()
+            olse = m + np.log(np.exp(s - m).sum())
+            assert abs(lse[r] - olse) <= 1e-4 * max(1.0, abs(olse))
+            assert abs(pmax[r] - p.max()) <= 1e-3 * max(1.0, abs(p.max()))
+            oa = int(np.argmax(p))
+            if arg[r] != oa:
+                assert p[oa] - p[arg[r]] < 1e-3 * (1 + abs(p[oa]))
+    say(f"group summary B={B} G={G}: ok")
