@@ -415,8 +415,23 @@ def main():
         g_ms, _ = timer.run(gstep, max(20, n // 4))
         ab = algorithmic_bytes(wg["B"], wg["d"], wg["V"]) + wg["n_groups"] * wg["B"] * wg["d"] * 2
         sweep.append({"workload": "grouped", "B": wg["B"], "d": wg["d"], "V": wg["V"], "groups": wg["n_groups"],
-                      "us_per_step": round(g_ms * 1e3, 2), "GB_per_s": round(ab / (g_ms * 1e-3) / 1e9, 1),
+                      "launch": "one per group", "us_per_step": round(g_ms * 1e3, 2),
+                      "GB_per_s": round(ab / (g_ms * 1e-3) / 1e9, 1),
                       "pct_peak": round(100 * ab / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
+        log(f"sweep {sweep[-1]}")
+
+        # the same summaries for all groups in one launch, then the combine
+        def gstep1(i):
+            fs.fs_group_summaries(ctx, Hg, Wg[i % len(Wg)], 0, G, wg["T"], 0, i, out=summ)
+            fs.fs_group_combine(ctx, summ, 0, i, fs.FS_COMBINE_GUMBEL, out=outg)
+
+        timer.run(gstep1, 5)
+        g1_ms, _ = timer.run(gstep1, max(20, n // 4))
+        ab1 = algorithmic_bytes(wg["B"], wg["d"], wg["V"])
+        sweep.append({"workload": "grouped", "B": wg["B"], "d": wg["d"], "V": wg["V"], "groups": wg["n_groups"],
+                      "launch": "all groups in one", "us_per_step": round(g1_ms * 1e3, 2),
+                      "GB_per_s": round(ab1 / (g1_ms * 1e-3) / 1e9, 1),
+                      "pct_peak": round(100 * ab1 / (g1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
         log(f"sweep {sweep[-1]}")
         del weights["grouped"]
         result["sweep"] = sweep

@@ -170,6 +170,22 @@ int fs_group_summary(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, 
                      uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out,
                      int path);
 
+/* Summaries of n_groups consecutive groups of G ids each in one launch:
+ *   W [n_groups * G, d] bf16 (row stride ldw) holds the LM-head rows of global
+ *   ids [vocab_offset, vocab_offset + n_groups * G); out [n_groups, B]
+ *   (group-major) receives, for group k, what fs_group_summary returns for
+ *   W + k * G * ldw at vocab_offset + k * G.  For callers that hold several
+ *   groups at once (a vocabulary shard, or every group of a step): H is staged
+ *   once per pass over many groups' rows instead of once per group.
+ *   mask as in fs_group_summary (full-vocabulary words).
+ *   [arXiv 2603.15854 abstract: grouped variants for online and
+ *    tensor-parallel settings; readus.org summary, "Group Gumbel Max"]
+ * Requires G % 16 == 0, n_groups >= 1, vocab_offset % 32 == 0 and
+ * vocab_offset + n_groups * G < 2^31. */
+int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                       int B, int d, int64_t vocab_offset, int64_t G, int n_groups, float temperature, uint64_t seed,
+                       uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out, int path);
+
 /* Combine per-group summaries s [n_groups, B] (group-major) into one sample
  * per row.
  *   FS_COMBINE_GUMBEL: k* = argmax_k (lse_k + g'_k) with g'_k the Gumbel

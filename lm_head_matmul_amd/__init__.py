@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     fs_fmms_sample_multi,
     fs_fmms_tiling,
     fs_group_combine,
+    fs_group_summaries,
     fs_group_summary,
     fs_last_error,
     fs_softmax_sample,

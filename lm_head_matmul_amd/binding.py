@@ -46,6 +46,8 @@ SIGNATURES = {
                                _I]),
     "fs_softmax_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _P, _P, _I64, _I]),
     "fs_group_summary": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _F, _U64, _U64, _P, _I64, _P, _I]),
+    "fs_group_summaries": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _I, _F, _U64, _U64, _P, _I64, _P,
+                                _I]),
     "fs_group_combine": (_I, [_P, _P, _P, _I, _I, _U64, _U64, _I, _P]),
     "fs_debug_philox": (_I, [_P, _P, _U64, _U64, _I, _I64, _I64, _P, _P]),
     "fs_debug_gumbel_bits": (_I, [_P, _P, _U64, _I64, _P]),
@@ -227,6 +229,26 @@ def fs_group_summary(ctx: int, H: torch.Tensor, W_group: torch.Tensor, vocab_off
     mptr, ldm = _mask_args(mask)
     _check(_lib.fs_group_summary(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W_group.data_ptr(), ldw, B, d,
                                  vocab_offset, G, float(temperature), seed, step, mptr, ldm, out.data_ptr(), path))
+    return out
+
+
+def fs_group_summaries(ctx: int, H: torch.Tensor, W: torch.Tensor, vocab_offset: int, group_size: int,
+                       temperature: float, seed: int, step: int, mask: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None, path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Summaries of the W.shape[0] // group_size consecutive groups of W: [n_groups, B, 3] int32 records."""
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if group_size < 1 or V % group_size != 0:
+        raise ValueError("W's rows must be a whole number of groups")
+    n_groups = V // group_size
+    if out is None:
+        out = torch.empty((n_groups, B, 3), dtype=torch.int32, device=H.device)
+    mptr, ldm = _mask_args(mask)
+    _check(_lib.fs_group_summaries(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, vocab_offset,
+                                   group_size, n_groups, float(temperature), seed, step, mptr, ldm, out.data_ptr(),
+                                   path))
     return out
 
 

@@ -542,6 +542,45 @@ int fs_group_summary(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, 
   });
 }
 
+int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                       int B, int d, int64_t vocab_offset, int64_t G, int n_groups, float temperature, uint64_t seed,
+                       uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out, int path) {
+  if (vocab_offset < 0 || vocab_offset % 32 != 0)
+    return fail(FS_ERR_INVALID_ARG, "vocab_offset=%lld must be a non-negative multiple of 32", (long long)vocab_offset);
+  if (n_groups < 1) return fail(FS_ERR_INVALID_ARG, "n_groups=%d must be >= 1", n_groups);
+  if (G < 16 || G % 16 != 0) return fail(FS_ERR_INVALID_ARG, "G=%lld must be a positive multiple of 16", (long long)G);
+  const int64_t Vall = G * n_groups;
+  if (vocab_offset + Vall >= ((int64_t)1 << 31))
+    return fail(FS_ERR_INVALID_ARG, "vocab_offset + n_groups * G must be < 2^31");
+  int rc = check_operands(ctx, H, ldh, W, ldw, B, d, Vall, temperature, mask, ldm, vocab_offset + Vall);
+  if (rc != FS_OK) return rc;
+  if (!out) return fail(FS_ERR_INVALID_ARG, "out is NULL");
+  if (path < FS_PATH_AUTO || path > FS_PATH_MFMA) return fail(FS_ERR_INVALID_ARG, "unknown path %d", path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  // launches of up to max_tiles groups, the context's tiles shared evenly
+  // among them (a tile never straddles two groups)
+  const int64_t gblocks = G / 16;
+  for (int g0 = 0; g0 < n_groups; g0 += ctx->max_tiles) {
+    const int ng = (n_groups - g0) < ctx->max_tiles ? (n_groups - g0) : ctx->max_tiles;
+    int64_t tpg = ctx->max_tiles / ng;
+    if (tpg > gblocks) tpg = gblocks;
+    fsk::StreamParams p;
+    fill_common(p, ctx, H, ldh, W + (int64_t)g0 * G * ldw, ldw, B, d, G * ng, temperature, seed, step, mask, ldm);
+    p.vocab_offset = vocab_offset + (int64_t)g0 * G;
+    p.group_tiles = (int)tpg;
+    p.group_blocks = gblocks;
+    p.n_tiles = (int)(tpg * ng);
+    p.n_mblocks = gblocks * ng;
+    p.group_out_stride = B;
+    rc = run_stream_chunks(p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
+      c.out_sum = reinterpret_cast<fsk::GroupSummary*>(out + (int64_t)g0 * B + r0);
+    });
+    if (rc != FS_OK) return rc;
+  }
+  return FS_OK;
+}
+
 int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int n_groups, int B, uint64_t seed,
                      uint64_t step, int mode, int32_t* out_idx) {
   if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");

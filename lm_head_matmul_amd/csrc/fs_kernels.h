@@ -31,6 +31,11 @@ struct StreamParams {
   // samples == 1, batch row b is H row b.
   int samples;
   int vrow0;
+  // Several vocabulary groups in one launch: group_tiles > 0 tiles per group,
+  // each group group_blocks 16-row blocks long; tiles never straddle groups.
+  int group_tiles;
+  int64_t group_blocks;
+  int64_t group_out_stride;  // summaries between consecutive groups in out_sum
   float inv_t;
   uint32_t seed_lo, seed_hi, step_lo, step_hi;
   const uint32_t* mask;  // [B, ldm] words or null

@@ -807,13 +807,19 @@ hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi
       e = launch_stream_epi<EPI_FLAT>(p, cfg, stream);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_tiles_kernel<EPI_FLAT>, rgrid, dim3(kThreads), 0, stream, p.B, p.n_tiles, p.ws_val,
-                         p.ws_idx, nullptr, nullptr, p.out_idx, nullptr);
+                         p.ws_idx, nullptr, nullptr, p.out_idx, nullptr, p.n_tiles, (int64_t)0);
       return hipGetLastError();
     case EPI_GROUP:
       e = launch_stream_epi<EPI_GROUP>(p, cfg, stream);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(reduce_tiles_kernel<EPI_GROUP>, rgrid, dim3(kThreads), 0, stream, p.B, p.n_tiles, p.ws_val,
-                         p.ws_idx, p.ws_m, p.ws_s, nullptr, p.out_sum);
+      if (p.group_tiles > 0) {  // one summary per group: out_sum is [groups][out_stride]
+        const dim3 ggrid((p.B + kWaves - 1) / kWaves, p.n_tiles / p.group_tiles);
+        hipLaunchKernelGGL(reduce_tiles_kernel<EPI_GROUP>, ggrid, dim3(kThreads), 0, stream, p.B, p.n_tiles,
+                           p.ws_val, p.ws_idx, p.ws_m, p.ws_s, nullptr, p.out_sum, p.group_tiles, p.group_out_stride);
+      } else {
+        hipLaunchKernelGGL(reduce_tiles_kernel<EPI_GROUP>, rgrid, dim3(kThreads), 0, stream, p.B, p.n_tiles,
+                           p.ws_val, p.ws_idx, p.ws_m, p.ws_s, nullptr, p.out_sum, p.n_tiles, (int64_t)0);
+      }
       return hipGetLastError();
     case EPI_STORE: return launch_stream_epi<EPI_STORE>(p, cfg, stream);
     default: return hipErrorInvalidValue;
@@ -825,7 +831,7 @@ hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_tiles_kernel<EPI_FLAT>, dim3((p.B + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, p.B,
-                     p.n_tiles, p.ws_val, p.ws_idx, nullptr, nullptr, p.out_idx, nullptr);
+                     p.n_tiles, p.ws_val, p.ws_idx, nullptr, nullptr, p.out_idx, nullptr, p.n_tiles, (int64_t)0);
   return hipGetLastError();
 }
 

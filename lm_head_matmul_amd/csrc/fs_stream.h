@@ -38,18 +38,21 @@ namespace fsk {
 // entries.  [FlashSampling, arXiv 2603.15854, section 3: the stage-2 reduction
 // over tiles]
 // ---------------------------------------------------------------------------
+// With several groups per launch (gridDim.y groups of tpg tiles each), group
+// g reduces tiles [g * tpg, (g + 1) * tpg) into out_sum[g * out_stride + b].
 template <int EPI>
 __global__ void __launch_bounds__(kThreads)
     reduce_tiles_kernel(const int B, const int n_tiles, const float* __restrict__ ws_val,
                         const int32_t* __restrict__ ws_idx, const float* __restrict__ ws_m,
                         const float* __restrict__ ws_s, int32_t* __restrict__ out_idx,
-                        GroupSummary* __restrict__ out_sum) {
+                        GroupSummary* __restrict__ out_sum, const int tpg, const int64_t out_stride) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (b >= B) return;
+  const int t0 = blockIdx.y * tpg;
   float v = -INFINITY, m = -INFINITY, s = 0.0f;
   int32_t i = -1;
-  for (int t = lane; t < n_tiles; t += 64) {
+  for (int t = t0 + lane; t < t0 + tpg; t += 64) {
     const int64_t o = (int64_t)b * n_tiles + t;
     merge_best(v, i, ws_val[o], ws_idx[o]);
     if (EPI == EPI_GROUP) lse_merge(m, s, ws_m[o], ws_s[o]);
@@ -71,7 +74,7 @@ __global__ void __launch_bounds__(kThreads)
       g.lse = (m == -INFINITY) ? -INFINITY : m + logf(s);
       g.pmax = v;
       g.arg = i;
-      out_sum[b] = g;
+      out_sum[(int64_t)blockIdx.y * out_stride + b] = g;
     } else {
       out_idx[b] = i;
     }
@@ -115,8 +118,14 @@ struct TileRange {
 
 __device__ __forceinline__ TileRange tile_range(const StreamParams& p) {
   TileRange t;
-  t.mb_lo = (int64_t)blockIdx.x * p.n_mblocks / p.n_tiles;
-  t.mb_hi = (int64_t)(blockIdx.x + 1) * p.n_mblocks / p.n_tiles;
+  if (p.group_tiles > 0) {  // balanced inside each group
+    const int g = blockIdx.x / p.group_tiles, j = blockIdx.x - g * p.group_tiles;
+    t.mb_lo = (int64_t)g * p.group_blocks + (int64_t)j * p.group_blocks / p.group_tiles;
+    t.mb_hi = (int64_t)g * p.group_blocks + (int64_t)(j + 1) * p.group_blocks / p.group_tiles;
+  } else {
+    t.mb_lo = (int64_t)blockIdx.x * p.n_mblocks / p.n_tiles;
+    t.mb_hi = (int64_t)(blockIdx.x + 1) * p.n_mblocks / p.n_tiles;
+  }
   t.rounds = (int)((t.mb_hi - t.mb_lo + kWaves - 1) / kWaves);
   return t;
 }

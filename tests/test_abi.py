@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ["fs_create", "fs_destroy", "fs_last_error", "fs_fmms_tiling", "fs_fmms_sample",
-                     "fs_fmms_sample_multi", "fs_unfused_sample", "fs_softmax_sample", "fs_group_summary", "fs_group_combine", "fs_debug_philox",
+                     "fs_fmms_sample_multi", "fs_unfused_sample", "fs_softmax_sample", "fs_group_summaries", "fs_group_summary", "fs_group_combine", "fs_debug_philox",
                      "fs_debug_gumbel_bits", "fs_debug_gumbel_scan"]:
         assert required in names
 

@@ -324,3 +324,64 @@ def test_grouped_summaries_and_combine(fs, ctx, B, d, G, n_groups, path):
         for k, b in np.argwhere(arg != oarg):
             p = oracle.perturbed_row(L[b], T, seed, step, int(b), mask_row=mask[b])
             assert p[oarg[k, b]] - p[arg[k, b]] < 1e-3 * (1 + abs(float(p[oarg[k, b]])))
+
+
+@pytest.mark.parametrize("B,d,G,n_groups,path", [
+    (6, 256, 512, 8, 0),      # more groups than one tile each would need
+    (64, 768, 1024, 4, 0),    # four batch blocks
+    (3, 520, 48, 9, 0),       # groups not a multiple of 32 ids (offsets cross mask words)
+    (5, 4096, 2000, 3, 2),    # chunked H, forced MFMA path
+])
+def test_group_summaries_in_one_launch(fs, ctx, B, d, G, n_groups, path):
+    # fs_group_summaries over consecutive groups equals the oracle's per-group
+    # summaries (and hence fs_group_summary called group by group)
+    import torch
+
+    V = G * n_groups
+    say(f"group summaries in one launch B={B} d={d} G={G} groups={n_groups} path={path}")
+    H = synth.normal_bf16(B, d, seed=19)
+    W = synth.normal_bf16(V, d, seed=20, std=1.5 / math.sqrt(d))
+    allowed = np.random.default_rng(21).random((B, V)) >= 0.25
+    allowed[1] = False
+    mask = synth.pack_mask(allowed)
+    L = oracle.logits(H, W)
+    Hd, Wd, md = dev_bf16(H), dev_bf16(W), dev_words(mask)
+    T, seed = 0.9, 78
+    for step in range(3):
+        summ = fs.fs_group_summaries(ctx, Hd, Wd, 0, G, T, seed, step, mask=md, path=path)
+        flat = fs.fs_fmms_sample(ctx, Hd, Wd, T, seed, step, mask=md, path=path)
+        comb_m = fs.fs_group_combine(ctx, summ, seed, step, fs.FS_COMBINE_MAX)
+        _sync()
+        assert torch.equal(comb_m, flat), "max-combine must equal the flat sample"
+        lse, pmax, arg = (x.cpu().numpy() for x in fs.summary_views(summ))
+        for k in range(n_groups):
+            olse, opmax, oarg = oracle.group_summary(L, k * G, G, T, seed, step, mask=mask)
+            fin = np.isfinite(olse)
+            assert np.array_equal(fin, np.isfinite(lse[k])) and np.all(arg[k][~fin] == -1)
+            assert np.all(np.abs(lse[k][fin] - olse[fin]) <= 1e-4 * np.maximum(1, np.abs(olse[fin])))
+            assert np.all(np.abs(pmax[k][fin] - opmax[fin]) <= 1e-3 * np.maximum(1, np.abs(opmax[fin])))
+            for b in np.flatnonzero(arg[k] != oarg):
+                p = oracle.perturbed_row(L[b], T, seed, step, int(b), mask_row=mask[b])
+                assert p[oarg[b]] - p[arg[k, b]] < 1e-3 * (1 + abs(float(p[oarg[b]])))
+
+
+def test_group_summaries_match_group_by_group_calls(fs, ctx):
+    import torch
+
+    B, d, G, n_groups = 9, 512, 4096, 5
+    H = synth.normal_bf16(B, d, seed=22)
+    W = synth.normal_bf16(G * n_groups, d, seed=23, std=0.08)
+    Hd, Wd = dev_bf16(H), dev_bf16(W)
+    one = fs.fs_group_summaries(ctx, Hd, Wd, 32 * 7, G, 1.0, 5, 2)
+    each = torch.empty_like(one)
+    for k in range(n_groups):
+        fs.fs_group_summary(ctx, Hd, Wd[k * G:(k + 1) * G], 32 * 7 + k * G, 1.0, 5, 2, out=each[k])
+    _sync()
+    # the two tilings may run different kernel forms (fp32 sums in another k
+    # order), so maxima agree to rounding and ids up to near-ties
+    a = [x.cpu().numpy() for x in fs.summary_views(one)]
+    b = [x.cpu().numpy() for x in fs.summary_views(each)]
+    assert np.allclose(a[0], b[0], rtol=1e-5, atol=1e-5)
+    assert np.allclose(a[1], b[1], rtol=1e-5, atol=1e-5)
+    diff = a[2] != b[2]
+    assert diff.mean() <= 1e-3 + 1e-9 or np.all(np.abs(a[1][diff] - b[1][diff]) < 1e-3 * (1 + np.abs(b[1][diff])))
