@@ -404,9 +404,9 @@ __device__ __forceinline__ void w_load8(const StreamParams& p, const TileRange& 
 // next round).  The loop body has no data-dependent branches, so the
 // compiler's wait counters stay exact and no prefetch is ever drained.
 // ---------------------------------------------------------------------------
-template <int U, bool RESIDENT, int LAYOUT, class Body, class RoundEnd>
+template <int U, bool RESIDENT, int LAYOUT, class Body, class RoundEnd, class Pre>
 __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const TileRange& tr, unsigned char* smem,
-                                                   Body&& body, RoundEnd&& round_end) {
+                                                   Body&& body, RoundEnd&& round_end, Pre&& pre) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int nsub = p.nsub, ngrp = nsub / U;
@@ -433,6 +433,16 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
     }
   };
 
+  // The first W items go out before anything else: their latency overlaps the
+  // kernel's own staging (pre: mask words, noise table) and H's.
+  u32x4_t buf[U][8];
+#pragma unroll
+  for (int k = 0; k < U - 1; ++k) {
+    load(buf[k], lr, lsb);
+    advance();
+  }
+  pre();
+
   // Chunked H (chunks of U = 2 sub-blocks, 1 KB per row): chunks are copied
   // straight into LDS (h_chunk_dma), the zero row of both buffers once here.
   static_assert(RESIDENT || U == 2, "chunked H in the fast driver: two sub-blocks per chunk");
@@ -449,12 +459,6 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
   }
   __syncthreads();
 
-  u32x4_t buf[U][8];
-#pragma unroll
-  for (int k = 0; k < U - 1; ++k) {
-    load(buf[k], lr, lsb);
-    advance();
-  }
   int cc = 0;  // chunks consumed (chunked H: one chunk per group)
   for (int r = 0; r < tr.rounds; ++r) {
     for (int g = 0; g < ngrp; ++g) {
@@ -489,9 +493,9 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
 // General driver: any d (k tail clamped into the row's last chunk, which meets
 // zeros in the staged H), any chunking, two register buffers.  Conditions are
 // evaluated per sub-block.
-template <bool RESIDENT, int LAYOUT, class Body, class RoundEnd>
+template <bool RESIDENT, int LAYOUT, class Body, class RoundEnd, class Pre>
 __device__ __forceinline__ void stream_driver_general(const StreamParams& p, const TileRange& tr, unsigned char* smem,
-                                                      Body&& body, RoundEnd&& round_end) {
+                                                      Body&& body, RoundEnd&& round_end, Pre&& pre) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int nsub = p.nsub, d = p.d;
@@ -499,6 +503,7 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
   const int nchunk = RESIDENT ? 1 : p.nchunk;
   const int bufbytes = p.h_rows * p.h_rowstride;
   if (tr.rounds == 0) return;
+  pre();
 
   auto load = [&](u32x4_t (&buf)[8], int r, int sb) {
     const uint16_t* base = w_row(p, tr, tr.mb_lo + (int64_t)r * kWaves + wave, l16);
@@ -582,13 +587,13 @@ __device__ __forceinline__ void stream_driver_general(const StreamParams& p, con
   }
 }
 
-template <bool FAST, bool RESIDENT, int RING, int LAYOUT, class Body, class RoundEnd>
+template <bool FAST, bool RESIDENT, int RING, int LAYOUT, class Body, class RoundEnd, class Pre>
 __device__ __forceinline__ void stream_driver(const StreamParams& p, const TileRange& tr, unsigned char* smem,
-                                              Body&& body, RoundEnd&& round_end) {
+                                              Body&& body, RoundEnd&& round_end, Pre&& pre) {
   if (FAST)
-    stream_driver_fast<RING, RESIDENT, LAYOUT>(p, tr, smem, body, round_end);
+    stream_driver_fast<RING, RESIDENT, LAYOUT>(p, tr, smem, body, round_end, pre);
   else
-    stream_driver_general<RESIDENT, LAYOUT>(p, tr, smem, body, round_end);
+    stream_driver_general<RESIDENT, LAYOUT>(p, tr, smem, body, round_end, pre);
 }
 
 // End of an MFMA streaming kernel: reduce each wave's maximizers over its four
@@ -658,9 +663,12 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   const int rs = p.h_rowstride;
   uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
   const int64_t mw_lo = mask_w_lo(p, tr);
-  if (MASKED) mask_stage(p, tr, mask_lds);  // made visible by the driver's first barrier
   const float* noise_lds = (const float*)(smem + p.noise_lds_off);
-  if (EPI != EPI_STORE && NOISE_LDS) noise_stage(p, tr, (float*)noise_lds);  // ditto
+  // staged by the driver once the first W loads are out, visible after its first barrier
+  auto pre = [&]() {
+    if (MASKED) mask_stage(p, tr, mask_lds);
+    if (EPI != EPI_STORE && NOISE_LDS) noise_stage(p, tr, (float*)noise_lds);
+  };
   // H row of this lane in each 16-wide batch block (padding lanes read the zero row)
   int hoff[NB];
 #pragma unroll
@@ -769,7 +777,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING, LAYOUT>(p, tr, smem, body, round_end);
+  stream_driver<FAST, RESIDENT, RING, LAYOUT>(p, tr, smem, body, round_end, pre);
   if (kDefer && tr.rounds > 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) finish_nb(tr.rounds - 1, nb);
@@ -1011,7 +1019,9 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
   const int rs = p.h_rowstride;
   uint32_t* mask_lds = (uint32_t*)(smem + p.mask_lds_off);
   const int64_t mw_lo = mask_w_lo(p, tr);
-  if (MASKED) mask_stage(p, tr, mask_lds);
+  auto pre = [&]() {
+    if (MASKED) mask_stage(p, tr, mask_lds);
+  };
 
   float bv = -INFINITY, lm = -INFINITY, ls = 0.0f;
   int32_t bi = -1;
@@ -1087,7 +1097,7 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING, kLayoutDot>(p, tr, smem, body, round_end);
+  stream_driver<FAST, RESIDENT, RING, kLayoutDot>(p, tr, smem, body, round_end, pre);
   if (tr.rounds > 0) finish_round(tr.rounds - 1);
   if (EPI == EPI_STORE) return;
 
