@@ -37,6 +37,8 @@ struct fs_ctx {
   int32_t* topk_cand_n;
   float* topk_seg_val;
   int32_t* topk_seg_idx;
+  int32_t* topk_bound;
+  uint32_t* topk_arrive;
   // conventional comparator: [max_B][kCdfMaxSeg] segment max, sum of exp, sum of probabilities
   float* cdf_ws;
 };
@@ -226,14 +228,19 @@ int launch_topk(const fs_ctx* ctx, const float* logits, int64_t ldl, int rows, i
   q.cand_n = ctx->topk_cand_n;
   q.seg_val = ctx->topk_seg_val;
   q.seg_idx = ctx->topk_seg_idx;
+  q.bound = ctx->topk_bound;
+  q.arrive_hist = ctx->topk_arrive;
+  q.arrive_coll = ctx->topk_arrive + ctx->topk_rows;
   // rows are processed in chunks of the workspace's topk_rows; each row is split
-  // into segments so that a chunk launches about 2048 workgroups, with segments
-  // of at least 512 quads
+  // into segments so that a chunk launches about 512 workgroups, with segments
+  // of at least 2048 quads: each workgroup's fixed latency (a device-scope
+  // round trip to count its arrival) then weighs less than its stretch of the
+  // scores (measured best on MI355X at 1 to 64 rows of 151936 scores)
   for (int c0 = 0; c0 < rows; c0 += ctx->topk_rows) {
     const int n = (rows - c0) < ctx->topk_rows ? (rows - c0) : ctx->topk_rows;
     const int64_t nq = (V + 3) / 4;
-    int64_t seg = 2048 / n;
-    if (seg > nq / 512) seg = nq / 512;
+    int64_t seg = 512 / n;
+    if (seg > nq / 2048) seg = nq / 2048;
     if (seg > fsk::kTopkMaxSeg) seg = fsk::kTopkMaxSeg;
     if (seg < 1) seg = 1;
     q.logits = logits + (int64_t)c0 * ldl;
@@ -313,10 +320,11 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
       return hip_fail(e, "hipMalloc(top-k workspace)");
     }
     // selection workspace: cand [rows][cap] u64, hist [rows][bins] u32, seg_val / seg_idx
-    // [rows][max_seg], cand_n [rows]; hist and cand_n start at zero and every call
-    // leaves them at zero
+    // [rows][max_seg], cand_n [rows], bound [rows][4], two arrival counters [rows];
+    // hist, cand_n and the counters start at zero and every call leaves them at zero
     const size_t R = (size_t)c->topk_rows;
-    const size_t sel = R * fsk::kTopkCap * 8 + R * fsk::kTopkBins * 4 + R * fsk::kTopkMaxSeg * 8 + R * 4;
+    const size_t sel =
+        R * fsk::kTopkCap * 8 + R * fsk::kTopkBins * 4 + R * fsk::kTopkMaxSeg * 8 + R * 4 + R * 16 + R * 8;
     e = hipMalloc(&c->topk_sel, sel);
     if (e == hipSuccess) e = hipMemset(c->topk_sel, 0, sel);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -334,6 +342,8 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     c->topk_seg_val = (float*)(t + R * fsk::kTopkCap * 8 + R * fsk::kTopkBins * 4);
     c->topk_seg_idx = (int32_t*)(c->topk_seg_val + R * fsk::kTopkMaxSeg);
     c->topk_cand_n = (int32_t*)(c->topk_seg_idx + R * fsk::kTopkMaxSeg);
+    c->topk_bound = c->topk_cand_n + R;
+    c->topk_arrive = (uint32_t*)(c->topk_bound + 4 * R);
   }
   *out = c;
   return FS_OK;

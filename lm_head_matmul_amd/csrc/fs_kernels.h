@@ -102,6 +102,9 @@ struct TopkParams {
   int32_t* cand_n;     // [B] candidate counts (zero)
   float* seg_val;      // [B][kTopkMaxSeg] segment maximizers
   int32_t* seg_idx;
+  int32_t* bound;          // [B][4] row boundary: bin, count above, count inside, total
+  uint32_t* arrive_hist;   // [B] arrival counters of the two launches (zero)
+  uint32_t* arrive_coll;
 };
 
 // Conventional comparator (softmax, prefix sum, inverse-CDF search) over
@@ -162,7 +165,7 @@ constexpr int kouter_max_rounds(int epi, int nb, bool masked) {
 }
 constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
 constexpr int kTopkBins = 4096;    // first-level bins of the top-k radix select (key bits 31..20)
-constexpr int kTopkCap = 4096;     // boundary-bin ids the segment-parallel selection gathers per row
+constexpr int kTopkCap = 2048;     // boundary-bin ids the segment-parallel selection gathers per row
 constexpr int kTopkMaxSeg = 64;    // segments per row in the top-k launches
 constexpr int kCdfMaxSeg = 64;     // segments per row in the comparator's launches
 

@@ -71,21 +71,31 @@ __global__ void __launch_bounds__(kThreads) sample_logits_kernel(const SamplePar
 //
 // Keys are order-preserving 32-bit images of the scores; the boundary is found
 // by a most-significant-digit radix select whose first level histograms key
-// bits 31..20.  Three launches per batch chunk, each row split into segments:
-//   1. histogram: every (segment, row) workgroup counts its keys in LDS and adds
-//      the non-zero bins into the row's histogram in global memory;
-//   2. collect: every (segment, row) workgroup reads the row's histogram, finds
-//      the boundary bin (the bin where the count from the top reaches k), takes
-//      the Gumbel-max over its ids above that bin, and appends its ids inside
-//      the bin to the row's candidate list;
-//   3. finish, one workgroup per row: sorts the candidates by (key desc, id asc),
-//      perturbs the first k - (count above) of them and merges them with the
-//      segments' maximizers; it then clears the row's histogram and count for
-//      the next call.
+// bits 31..20.  Two launches per batch chunk, each row split into segments:
+//   1. histogram: every (segment, row) workgroup counts its keys in LDS, finds
+//      its own boundary bin (where its count from the top reaches k) and adds
+//      its non-zero bins from there up into the row's histogram in global
+//      memory.  The row's last workgroup to arrive (a per-row arrival counter)
+//      reads the histogram back, stores the row's boundary -- the bin where the
+//      count from the top reaches k, the count above that bin, the count inside
+//      it and the total -- and leaves the histogram and the counter at zero for
+//      the next call;
+//   2. collect: every (segment, row) workgroup takes the Gumbel-max over its
+//      ids above the boundary bin and appends its ids inside the bin to the
+//      row's candidate list.  The row's last workgroup to arrive ranks the
+//      candidates by (key desc, id asc), perturbs the first k - above of them,
+//      merges them with the segments' maximizers, writes the sample and leaves
+//      the candidate count and the counter at zero.
+// What one workgroup hands to a row's last one goes through device-scope
+// atomics (histogram adds, candidate and maximizer stores, their loads), which
+// are coherent across the chip's L2 caches; every thread waits for its own to
+// complete before the workgroup counts its arrival.  A device-scope fence would
+// do the same by writing back and invalidating whole L2 caches, which costs
+// far more than the pass.
 // A boundary bin holding more than kTopkCap ids (very narrow score ranges) is
-// resolved by the finish workgroup alone: it refines the bin on key bits 19..8
-// and 7..0 and, if more than kTopkCap ids share the exact boundary key, keeps
-// the lowest of them by a pass in id order.
+// resolved by the last collect workgroup alone: it refines the bin on key bits
+// 19..8 and 7..0 and, if more than kTopkCap ids share the exact boundary key,
+// keeps the lowest of them by a pass in id order.
 // ---------------------------------------------------------------------------
 // Order-preserving key of a score, with -0 folded onto +0 (they compare equal).
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -93,15 +103,30 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Device-scope loads and stores of the words workgroups hand to each other.
+template <class T>
+__device__ __forceinline__ void dev_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T dev_load(T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+static_assert(kTopkCap * 8 == kTopkBins * 4, "candidate list and refinement histogram share LDS");
+static_assert(kTopkBins % kThreads == 0, "whole runs of bins per thread");
+
 struct TopkShared {
-  uint32_t hist[kTopkBins];
-  uint64_t cand[kTopkCap];
-  int bin, above, inbin, total, ncand, run;
+  union {
+    uint32_t hist[kTopkBins];  // refinement levels of a row resolved alone
+    uint64_t cand[kTopkCap];   // boundary candidates (key << 32 | ~id)
+  };
+  int bin, above, inbin, total, ncand, run, last;
   float red_v[kWaves];
   int32_t red_i[kWaves];
 };
 
-// Wave 0: the boundary of a histogram of nbins bins (counts from the top):
+// Wave 0: the boundary of an LDS histogram of nbins bins (counts from the top):
 // total count, the bin where the running count from the top reaches `need`,
 // the count above that bin and the count inside it.  If total < need the bin
 // fields are left unset.
@@ -135,6 +160,58 @@ __device__ __forceinline__ void topk_boundary(const uint32_t* h, int nbins, int 
   }
 }
 
+constexpr int kTopkPer = kTopkBins / kThreads;  // histogram bins per thread in the block-wide scans
+
+// The whole workgroup: boundary of a histogram whose bins are held kTopkPer to
+// a thread (thread t holds c[0..kTopkPer) of bins base .. base + kTopkPer - 1,
+// the ones that come t-th from the top), written as {bin, above, inbin, total}
+// to out ({-1, 0, 0, total} when total < need).  out is read after the
+// caller's next barrier; wsum is LDS scratch of kWaves words.
+__device__ __forceinline__ void topk_boundary_block(const uint32_t (&c)[kTopkPer], int base, int need, int32_t* wsum,
+                                                    int32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) local += (int)c[j];
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int s = wsum[w];
+    if (w < wave) incl += s;
+    total += s;
+  }
+  const int excl = incl - local;
+  if (tid == 0) {
+    out[3] = total;
+    if (total < need) {
+      out[0] = -1;
+      out[1] = 0;
+      out[2] = 0;
+    }
+  }
+  if (excl < need && incl >= need) {
+    int run = excl;
+#pragma unroll
+    for (int j = kTopkPer - 1; j >= 0; --j) {
+      const int n = (int)c[j];
+      if (run < need && run + n >= need) {
+        out[0] = base + j;
+        out[1] = run;
+        out[2] = n;
+      }
+      run += n;
+    }
+  }
+}
+
 // Workgroup maximizer; the result is valid in thread 0.
 __device__ __forceinline__ void topk_block_best(float& bv, int32_t& bi, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -154,7 +231,22 @@ __device__ __forceinline__ void topk_block_best(float& bv, int32_t& bi, TopkShar
     for (int w = 0; w < kWaves; ++w) merge_best(bv, bi, sh.red_v[w], sh.red_i[w]);
 }
 
-// Row view shared by the three launches.
+// Arrival of a workgroup at a per-row counter once its device-scope writes
+// have completed; true in every thread of the row's last workgroup, which may
+// then read them with device-scope loads.  The last one resets the counter.
+__device__ __forceinline__ bool topk_arrive_last(uint32_t* counter, int n, int& flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's atomics and stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const bool last = atomicAdd(counter, 1u) == (uint32_t)(n - 1);
+    if (last) dev_store(counter, 0u);
+    flag = last;
+  }
+  __syncthreads();
+  return flag != 0;
+}
+
+// Row view shared by the launches.
 struct TopkRow {
   const float* L;
   const uint32_t* M;
@@ -225,6 +317,9 @@ __device__ __forceinline__ void topk_segment(const TopkParams& p, int seg, int64
 
 __global__ void __launch_bounds__(kThreads) topk_hist_kernel(const TopkParams p) {
   __shared__ uint32_t hist[kTopkBins];
+  __shared__ int32_t wsum[kWaves];
+  __shared__ int32_t local_bound[4];
+  __shared__ int last;
   const int seg = blockIdx.x, b = blockIdx.y;
   const TopkRow row = topk_row(p, b);
   for (int i = threadIdx.x; i < kTopkBins; i += kThreads) hist[i] = 0;
@@ -233,47 +328,28 @@ __global__ void __launch_bounds__(kThreads) topk_hist_kernel(const TopkParams p)
   topk_segment(p, seg, q_lo, q_hi);
   topk_scan(row, q_lo, q_hi, [&](int, float, uint32_t key) { atomicAdd(&hist[key >> 20], 1u); });
   __syncthreads();
+  // Only the bins from this segment's own boundary up are added to the row's
+  // histogram: the row's boundary is never below a segment's (that segment
+  // alone has k ids from its boundary up), so every bin from the row's
+  // boundary up gets all its counts.  The row's total is exact when it is
+  // below k (no segment is cut then).
+  const int base = kTopkBins - kTopkPer * ((int)threadIdx.x + 1);
+  uint32_t c[kTopkPer];
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) c[j] = hist[base + j];
+  topk_boundary_block(c, base, p.top_k, wsum, local_bound);
+  __syncthreads();
+  const int floor_bin = local_bound[0] < 0 ? 0 : local_bound[0];
   uint32_t* gh = p.hist + (int64_t)b * kTopkBins;
-  for (int i = threadIdx.x; i < kTopkBins; i += kThreads)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
-}
-
-__global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams p) {
-  __shared__ TopkShared sh;
-  const int seg = blockIdx.x, b = blockIdx.y;
-  const TopkRow row = topk_row(p, b);
-  if (threadIdx.x < 64) topk_boundary(p.hist + (int64_t)b * kTopkBins, kTopkBins, p.top_k, sh);
-  __syncthreads();
-  const bool keep_all = sh.total <= p.top_k;
-  const uint32_t bin = keep_all ? 0u : (uint32_t)sh.bin;
-  const bool collect = !keep_all && sh.inbin <= kTopkCap;
-  float bv = -INFINITY;
-  int32_t bi = -1;
-  int64_t q_lo, q_hi;
-  topk_segment(p, seg, q_lo, q_hi);
-  if (threadIdx.x == 0) sh.ncand = 0;
-  __syncthreads();
-  // this segment's boundary candidates go to LDS first (at most the bin's count,
-  // <= kTopkCap), then to the row's list with one global atomic per workgroup
-  topk_scan(row, q_lo, q_hi, [&](int v, float s, uint32_t key) {
-    const uint32_t hi = key >> 20;
-    if (keep_all || hi > bin) {
-      topk_take(p, row, v, s, bv, bi);
-    } else if (collect && hi == bin) {
-      const int at = atomicAdd(&sh.ncand, 1);
-      sh.cand[at] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
-    }
-  });
-  topk_block_best(bv, bi, sh);  // its barriers also publish sh.ncand and sh.cand
-  const int n = sh.ncand;
-  if (threadIdx.x == 0) {
-    p.seg_val[(int64_t)b * kTopkMaxSeg + seg] = bv;
-    p.seg_idx[(int64_t)b * kTopkMaxSeg + seg] = bi;
-    sh.run = n > 0 ? atomicAdd(&p.cand_n[b], n) : 0;
-  }
-  __syncthreads();
-  uint64_t* cand = p.cand + (int64_t)b * kTopkCap + sh.run;
-  for (int i = threadIdx.x; i < n; i += kThreads) cand[i] = sh.cand[i];
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j)
+    if (base + j >= floor_bin && c[j]) atomicAdd(&gh[base + j], c[j]);
+  if (!topk_arrive_last(p.arrive_hist + b, p.n_seg, last)) return;
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) c[j] = dev_load(gh + base + j);
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) dev_store(gh + base + j, 0u);
+  topk_boundary_block(c, base, p.top_k, wsum, p.bound + 4 * (int64_t)b);
 }
 
 // Sorts sh.cand[0, n) descending (bitonic, padded with zeros to a power of 2).
@@ -391,29 +467,40 @@ __device__ void topk_row_alone(const TopkParams& p, const TopkRow& row, TopkShar
   }
 }
 
-__global__ void __launch_bounds__(kThreads) topk_finish_kernel(const TopkParams p) {
-  __shared__ TopkShared sh;
+// The last collect workgroup of a row: merges the segments' maximizers with
+// the perturbed first `need` boundary candidates and writes the row's sample.
+__device__ void topk_finish_row(const TopkParams& p, const TopkRow& row, int b, bool keep_all, int above, int inbin,
+                                TopkShared& sh) {
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const TopkRow row = topk_row(p, b);
-  uint32_t* gh = p.hist + (int64_t)b * kTopkBins;
-  if (tid < 64) topk_boundary(gh, kTopkBins, p.top_k, sh);
-  __syncthreads();
-  const bool keep_all = sh.total <= p.top_k;
-  const int need = keep_all ? 0 : p.top_k - sh.above;
-  const int inbin = keep_all ? 0 : sh.inbin;
   float bv = -INFINITY;
   int32_t bi = -1;
   if (keep_all || inbin <= kTopkCap) {
     for (int i = tid; i < p.n_seg; i += kThreads)
-      merge_best(bv, bi, p.seg_val[(int64_t)b * kTopkMaxSeg + i], p.seg_idx[(int64_t)b * kTopkMaxSeg + i]);
+      merge_best(bv, bi, dev_load(p.seg_val + (int64_t)b * kTopkMaxSeg + i),
+                 dev_load(p.seg_idx + (int64_t)b * kTopkMaxSeg + i));
     if (!keep_all) {
-      const uint64_t* cand = p.cand + (int64_t)b * kTopkCap;
-      for (int i = tid; i < inbin; i += kThreads) sh.cand[i] = cand[i];
-      topk_sort_desc(sh, inbin);  // begins with a barrier-separated fill
-      for (int i = tid; i < need; i += kThreads) {
-        const int v = cand_id(sh.cand[i]);
-        topk_take(p, row, v, row.score(v), bv, bi);
+      const int need = p.top_k - above;
+      uint64_t* cand = p.cand + (int64_t)b * kTopkCap;
+      if (inbin <= kThreads) {
+        // one candidate per thread, kept if fewer than `need` candidates rank above it
+        const uint64_t mine = tid < inbin ? dev_load(cand + tid) : 0ull;
+        if (tid < inbin) sh.cand[tid] = mine;
+        __syncthreads();
+        if (tid < inbin) {
+          int rank = 0;
+          for (int j = 0; j < inbin; ++j) rank += sh.cand[j] > mine ? 1 : 0;
+          if (rank < need) {
+            const int v = cand_id(mine);
+            topk_take(p, row, v, row.score(v), bv, bi);
+          }
+        }
+      } else {
+        for (int i = tid; i < inbin; i += kThreads) sh.cand[i] = dev_load(cand + i);
+        topk_sort_desc(sh, inbin);  // begins with a barrier-separated fill
+        for (int i = tid; i < need; i += kThreads) {
+          const int v = cand_id(sh.cand[i]);
+          topk_take(p, row, v, row.score(v), bv, bi);
+        }
       }
     }
   } else {
@@ -422,11 +509,51 @@ __global__ void __launch_bounds__(kThreads) topk_finish_kernel(const TopkParams 
   topk_block_best(bv, bi, sh);
   if (tid == 0) {
     p.out_idx[b] = bi;
-    p.cand_n[b] = 0;
+    dev_store(p.cand_n + b, 0);
   }
-  for (int i = tid; i < kTopkBins; i += kThreads) gh[i] = 0;  // wave 0 read it before the barriers above
 }
 
+__global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams p) {
+  __shared__ TopkShared sh;
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const TopkRow row = topk_row(p, b);
+  const int32_t* bd = p.bound + 4 * (int64_t)b;
+  const int bnd_bin = bd[0], above = bd[1], inbin = bd[2], total = bd[3];
+  const bool keep_all = total < p.top_k;  // the total is exact only then
+  const uint32_t bin = keep_all ? 0u : (uint32_t)bnd_bin;
+  const bool collect = !keep_all && inbin <= kTopkCap;
+  float bv = -INFINITY;
+  int32_t bi = -1;
+  int64_t q_lo, q_hi;
+  topk_segment(p, seg, q_lo, q_hi);
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  // this segment's boundary candidates go to LDS first (at most the bin's count,
+  // <= kTopkCap), then to the row's list with one global atomic per workgroup;
+  // a row whose bin is wider than that is left to its last workgroup
+  if (keep_all || collect)
+    topk_scan(row, q_lo, q_hi, [&](int v, float s, uint32_t key) {
+      const uint32_t hi = key >> 20;
+      if (keep_all || hi > bin) {
+        topk_take(p, row, v, s, bv, bi);
+      } else if (hi == bin) {
+        const int at = atomicAdd(&sh.ncand, 1);
+        sh.cand[at] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+      }
+    });
+  topk_block_best(bv, bi, sh);  // its barriers also publish sh.ncand and sh.cand
+  const int n = sh.ncand;
+  if (threadIdx.x == 0) {
+    dev_store(p.seg_val + (int64_t)b * kTopkMaxSeg + seg, bv);
+    dev_store(p.seg_idx + (int64_t)b * kTopkMaxSeg + seg, bi);
+    sh.run = n > 0 ? atomicAdd(&p.cand_n[b], n) : 0;
+  }
+  __syncthreads();
+  uint64_t* cand = p.cand + (int64_t)b * kTopkCap + sh.run;
+  for (int i = threadIdx.x; i < n; i += kThreads) dev_store(cand + i, sh.cand[i]);
+  if (!topk_arrive_last(p.arrive_coll + b, p.n_seg, sh.last)) return;
+  topk_finish_row(p, row, b, keep_all, above, inbin, sh);
+}
 // ---------------------------------------------------------------------------
 // Conventional comparator, not the method: the softmax pipeline the fused
 // sampler replaces [readus.org FlashSampling summary, the essay part: the
@@ -839,7 +966,6 @@ hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream) {
   const dim3 grid(p.n_seg, p.B);
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

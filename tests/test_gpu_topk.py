@@ -103,9 +103,10 @@ def test_topk_one_is_argmax(fs, ctx):
     assert np.all(ids == want[None, :])
 
 
-def test_topk_ties_at_boundary(fs, ctx):
+@pytest.mark.parametrize("V", [3000, 40000])  # one segment per row, several
+def test_topk_ties_at_boundary(fs, ctx, V):
     # integer logits: many exactly equal scores, the k-th value falls inside a tie group
-    B, d, V, k = 6, 256, 3000, 40
+    B, d, k = 6, 256, 40
     H = synth.small_int_bf16(B, d, seed=25)
     W = synth.small_int_bf16(V, d, seed=26, lo=-1, hi=1)
     ids, L = _check(fs, ctx, H, W, 1.0, 5, 40, k, label="ties")
@@ -132,10 +133,11 @@ def test_topk_with_mask(fs, ctx):
             assert np.all(allowed[b, ids[:, b]])
 
 
-def test_topk_all_scores_equal(fs, ctx):
+@pytest.mark.parametrize("V", [9000, 40000])
+def test_topk_all_scores_equal(fs, ctx, V):
     # every score is 0: the boundary holds all V equal keys (more than the
     # selection kernel gathers), so the k lowest ids are kept
-    B, d, V, k = 3, 256, 9000, 25
+    B, d, k = 3, 256, 25
     H = np.zeros((B, d), np.uint16)
     W = synth.normal_bf16(V, d, seed=31)
     ids, L = _check(fs, ctx, H, W, 1.0, 7, 30, k, label="all equal")
@@ -143,10 +145,11 @@ def test_topk_all_scores_equal(fs, ctx):
     assert np.all((ids >= 0) & (ids < k))
 
 
-def test_topk_narrow_score_range(fs, ctx):
+@pytest.mark.parametrize("V", [12000, 40000])
+def test_topk_narrow_score_range(fs, ctx, V):
     # scores within a few ulps of 1.0 for most ids: the first-level bin is too
     # wide for the candidate buffer and the selection refines it
-    B, d, V, k = 2, 256, 12000, 50
+    B, d, k = 2, 256, 50
     H = np.zeros((B, d), np.uint16)
     H[:, 0] = 0x3F80  # 1.0
     W = np.zeros((V, d), np.uint16)
@@ -157,3 +160,29 @@ def test_topk_narrow_score_range(fs, ctx):
     for b in range(B):
         order = np.lexsort((np.arange(V), -L[b].astype(np.float64)))
         assert set(ids[:, b].tolist()) <= set(order[:k].tolist())
+
+
+def test_topk_rows_held_by_one_segment(fs, ctx):
+    # a full-size row is split into segments, each adding to the row's
+    # histogram only its bins from its own k-th score up; masks that put all
+    # of a row's allowed ids in one stretch of the vocabulary check the cases
+    # where that cut matters: many, exactly k + 1, exactly k, and fewer than k
+    # allowed ids in one segment, k spread thinly over all segments, no mask
+    B, d, V, k = 6, 256, 40000, 50
+    H = synth.normal_bf16(B, d, seed=33)
+    W = synth.normal_bf16(V, d, seed=34, std=0.05)
+    allowed = np.zeros((B, V), bool)
+    allowed[0, 100:1100] = True
+    allowed[1, 300:300 + k + 1] = True
+    allowed[2, 39000:39000 + k] = True
+    allowed[3, 20000:20000 + k - 1] = True
+    allowed[4, ::V // k] = True
+    allowed[5] = True
+    mask = synth.pack_mask(allowed)
+    ids, L = _check(fs, ctx, H, W, 1.0, 9, 30, k, mask_np=mask, label="one-segment rows")
+    for b in range(B):
+        s = np.where(allowed[b], L[b].astype(np.float64), -np.inf)
+        order = np.lexsort((np.arange(V), -s))
+        kept = set(order[:min(k, int(allowed[b].sum()))].tolist())
+        assert set(ids[:, b].tolist()) <= kept, b
+    assert len(set(ids[:, 3].tolist())) > 10  # all k - 1 allowed ids stay in play
