@@ -152,7 +152,8 @@ constexpr int kMfmaMaxB = 64;
 // One load instruction of a wave touches 64, 16 or 32 cache lines.  The map
 // per kernel family is the measured best on gfx950.
 constexpr int kLayoutTable = 0;     // round-major kernel with the tile's noise table in LDS
-constexpr int kLayoutEpilogue = 1;  // round-major kernel, noise in the epilogue (and stored logits)
+constexpr int kLayoutEpilogue = 1;  // round-major kernel, noise in the epilogue
+constexpr int kLayoutStore = 0;     // round-major kernel storing the logits
 constexpr int kLayoutKouter = 1;    // chunk-outer kernel
 constexpr int kLayoutDot = 0;       // dot-product kernel
 // Rounds per pass of the chunk-outer kernel (accumulator sets a wave keeps in

@@ -655,7 +655,7 @@ __device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned
 template <int NB, int EPI, bool RESIDENT, bool FAST, bool MASKED, bool NOISE_LDS,
           int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
-  constexpr int LAYOUT = NOISE_LDS ? kLayoutTable : kLayoutEpilogue;
+  constexpr int LAYOUT = EPI == EPI_STORE ? kLayoutStore : NOISE_LDS ? kLayoutTable : kLayoutEpilogue;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
