@@ -229,12 +229,24 @@ __device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], c
 // (lane l carries bytes [16 l, 16 l + 16) of it).  Rows b < B only (wave
 // b % kWaves issues row b); the zero row is written once at kernel start.  The
 // loads retire in order with the W loads of the issuing wave.
+// The copies are a fixed, fully unrolled sequence of ROWS rows per wave (row b
+// of wave w is w + 8k), every one issued: rows past B repeat row B - 1, which
+// writes the same bytes to the same place.  A loop over b < B would leave the
+// compiler unable to count the loads in flight after it, and the next use of
+// any earlier load would then wait for all of them (vmcnt 0), draining the W
+// prefetch at every chunk; guarded copies leave branches that do the same.
+template <int ROWS>
 __device__ __forceinline__ void h_chunk_dma(const StreamParams& p, int cidx, unsigned char* buf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint16_t* src = p.H + cidx * 512 + lane * 8;
-  for (int b = wave; b < p.B; b += kWaves)
+#pragma unroll
+  for (int k = 0; k < ROWS; ++k) {
+    const int b0 = wave + k * kWaves;
+    const int b = b0 < p.B ? b0 : p.B - 1;
     __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)vrow_of(p, b).h * p.ldh),
                                      (__attribute__((address_space(3))) void*)(buf + b * p.h_rowstride), 16, 0, 0);
+  }
 }
 
 // The vocabulary mask of the tile, staged in LDS at kernel start: rows b < B,
@@ -454,7 +466,7 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
       *(u32x4_t*)(smem + row * p.h_rowstride + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t*)(smem + bufbytes + row * p.h_rowstride + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
     }
-    h_chunk_dma(p, 0, smem);
+    h_chunk_dma<kMfmaMaxB / kWaves>(p, 0, smem);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS copies have landed
   }
   __syncthreads();
@@ -469,7 +481,8 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
         // the chunk after this one (chunk index == group index) into the other
         // buffer; past the last group of the last round this copies chunk 0
         // once more, unused
-        if (!RESIDENT && k == 0) h_chunk_dma(p, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
+        if (!RESIDENT && k == 0)
+          h_chunk_dma<kMfmaMaxB / kWaves>(p, g + 1 < ngrp ? g + 1 : 0, smem + ((cc + 1) & 1) * bufbytes);
         // keep the loads above ahead of the compute below: the scheduler would
         // otherwise sink them under the MFMAs to save registers
         __builtin_amdgcn_sched_barrier(0);
@@ -905,7 +918,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
       *(u32x4_t*)(smem + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t*)(smem + bufbytes + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
     }
-    h_chunk_dma(p, 0, smem);
+    h_chunk_dma<2 * NB>(p, 0, smem);
     int64_t rowp[RM];  // the wave's block in each round of the pass
 #pragma unroll
     for (int r = 0; r < RM; ++r) rowp[r] = blk(0, r);
@@ -931,6 +944,11 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
         const int np = last_c && pass + 1 < npass ? pass + 1 : pass;
         const int64_t next_row = last_c ? blk(np, 0) : rowp[0];  // first item of the next chunk
         const int next_sb = last_c ? 0 : (c + 1) * 2;
+        // In the last chunk each round is finished right after its compute.  The
+        // finish is long ALU work, so the second sub-block of the next round is
+        // loaded into the buffer just freed before it: two items stay in flight
+        // through the finish instead of one, and that round skips its own load.
+        const bool early = EPI != EPI_STORE && last_c;
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
           if (r == RM - 1 && RM > 1 && !last_on) break;
@@ -939,7 +957,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
             // the W item after (r, sb): same round's next sub-block, the next
             // round's first one, or the first one of the next chunk / pass
             if (sb == 0) {
-              load(buf[1], rowp[r], c * 2 + 1);
+              if (!(early && r > 0)) load(buf[1], rowp[r], c * 2 + 1);
             } else if (r + 2 < RM || (r + 2 == RM && RM > 1)) {
               if (r + 2 == RM)  // the next round is the last one: it may be skipped
                 load(buf[0], last_on ? rowp[r + 1] : next_row, last_on ? c * 2 : next_sb);
@@ -948,7 +966,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
             } else {
               load(buf[0], next_row, next_sb);
             }
-            if (r == 0 && sb == 0) h_chunk_dma(p, nc, smem + ((cc + 1) & 1) * bufbytes);
+            if (r == 0 && sb == 0) h_chunk_dma<2 * NB>(p, nc, smem + ((cc + 1) & 1) * bufbytes);
             __builtin_amdgcn_sched_barrier(0);
             compute(buf[sb], hb + sb * 512, acc[r]);
           }
@@ -957,6 +975,8 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
           // the logits is cheap and is left to the end of the pass, which
           // keeps more rounds within the register budget)
           if (EPI != EPI_STORE && last_c) {
+            // round r + 1 runs in this chunk unless it is a skipped last round
+            if (r + 1 < RM && (r + 2 < RM || last_on)) load(buf[1], rowp[r + 1], c * 2 + 1);
             __builtin_amdgcn_sched_barrier(0);
             finish(pass, r, acc[r]);
 #pragma unroll
