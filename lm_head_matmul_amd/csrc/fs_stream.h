@@ -503,6 +503,86 @@ __device__ __forceinline__ void stream_driver_fast(const StreamParams& p, const 
   }
 }
 
+// Resident-H driver with blocks handed out on demand.  With H resident the
+// waves of a workgroup share nothing while they stream but H, the tile's noise
+// table and its mask words, so the tile's blocks need not be dealt in fixed
+// rounds: wave w starts on block mb_lo + w, and each further block comes from
+// a counter in LDS, taken as the wave starts its current block so that the
+// prefetch of the next block's first sub-block knows where to read.  (With a
+// fixed share per wave the second wave of each SIMD streamed at about half the
+// rate of the first on MI355X, and the last ~45% of a workgroup's time ran on
+// half of its waves.)
+// body(buf, hbase, sbc, pblk, t): compute sub-block sbc of the current block,
+// pblk being the wave's previous block (-1 before its second) whose epilogue
+// may be finished at step t; block_end(cblk, pblk): the current block's
+// accumulators are complete.  Returns the wave's last block, -1 if it had none.
+template <int U, int LAYOUT, class Body, class BlockEnd, class Pre>
+__device__ __forceinline__ int64_t stream_driver_dynamic(const StreamParams& p, const TileRange& tr,
+                                                         unsigned char* smem, int* next_blk, Body&& body,
+                                                         BlockEnd&& block_end, Pre&& pre) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int nsub = p.nsub, ngrp = nsub / U;
+  if (tr.rounds == 0) return -1;  // an empty tile (the whole workgroup)
+  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) {
+    const char* src = (const char*)(w_row(p, tr, mb, l16) + sb * 256) + lane_base<LAYOUT>(grp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) buf[e] = *(const u32x4_t*)(src + e * lane_step<LAYOUT>());
+  };
+  int64_t cur = tr.mb_lo + wave;  // the wave's current block
+  const bool any = cur < tr.mb_hi;
+  if (!any) cur = tr.mb_hi - 1;  // loads of a wave without blocks stay in the tile; none is used
+  int64_t nxt = -1;               // the block after the current one, -1 if none
+  int64_t lb = cur;               // next position to load
+  int lsb = 0;
+  auto advance = [&]() {
+    if (++lsb == nsub) {
+      if (nxt >= 0) {
+        lb = nxt;
+        lsb = 0;
+      } else {
+        lsb = nsub - 1;  // past the wave's last block: stay on its last sub-block
+      }
+    }
+  };
+
+  // the first W items go out before the kernel's own staging (pre) and H's
+  u32x4_t buf[U][8];
+#pragma unroll
+  for (int k = 0; k < U - 1; ++k) {
+    load(buf[k], lb, lsb);
+    advance();
+  }
+  pre();
+  h_stage_all(p, 0, smem);
+  if (threadIdx.x == 0) *next_blk = (int)(tr.mb_lo + kWaves);
+  __syncthreads();
+  if (!any) return -1;
+
+  int64_t pblk = -1;
+  for (;;) {
+    int got = 0;
+    if (lane == 0) got = atomicAdd(next_blk, 1);
+    got = __builtin_amdgcn_readfirstlane(got);
+    nxt = got < tr.mb_hi ? got : -1;
+    for (int g = 0; g < ngrp; ++g) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        load(buf[(k + U - 1) % U], lb, lsb);
+        advance();
+        // keep the loads above ahead of the compute below
+        __builtin_amdgcn_sched_barrier(0);
+        body(buf[k], smem, g * U + k, pblk, g * U + k);
+      }
+    }
+    block_end(cur, pblk);
+    pblk = cur;
+    if (nxt < 0) break;
+    cur = nxt;
+  }
+  return cur;
+}
+
 // General driver: any d (k tail clamped into the row's last chunk, which meets
 // zeros in the staged H), any chunking, two register buffers.  Conditions are
 // evaluated per sub-block.
@@ -735,10 +815,9 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
   };
 
-  // Finish N-block nb of the pending accumulators of round rnd.
-  auto finish_nb = [&](int rnd, int nb) {
-    const int64_t mbg = tr.mb_lo + (int64_t)rnd * kWaves + wave;
-    if (mbg >= tr.mb_hi) return;
+  // Finish N-block nb of the pending accumulators of block mbg.
+  auto finish_nb = [&](int64_t mbg, int nb) {
+    if (mbg < 0 || mbg >= tr.mb_hi) return;
     const int64_t v0 = mbg * 16 + grp * 4;
     const int b = nb * 16 + l16;
     if (b >= p.B) return;
@@ -762,22 +841,23 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
   };
 
-  // NB <= 2: deferred (see above).  NB = 4: the round is finished at its end
+  // NB <= 2: deferred (see above).  NB = 4: the block is finished at its end
   // (measured no slower, and it leaves the registers to the operand pipeline).
   constexpr bool kDefer = NB <= 2;
-  auto body = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc, int r, int t) {
+  // pblk: the wave's previous block (-1 if none); cblk: the block just completed
+  auto body_b = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc, int64_t pblk, int t) {
     compute(cur, hbase, sbc);
-    if (kDefer && r > 0 && t < NB) {
+    if (kDefer && pblk >= 0 && t < NB) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        if (nb == t) finish_nb(r - 1, nb);
+        if (nb == t) finish_nb(pblk, nb);
     }
   };
-  auto round_end = [&](int r) {
-    if (kDefer && r > 0 && p.nsub < NB) {  // fewer sub-blocks per round than N-blocks
+  auto block_end = [&](int64_t cblk, int64_t pblk) {
+    if (kDefer && pblk >= 0 && p.nsub < NB) {  // fewer sub-blocks per block than N-blocks
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        if (nb >= p.nsub) finish_nb(r - 1, nb);
+        if (nb >= p.nsub) finish_nb(pblk, nb);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -786,14 +866,27 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     }
     if (!kDefer) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) finish_nb(r, nb);
+      for (int nb = 0; nb < NB; ++nb) finish_nb(cblk, nb);
     }
   };
 
-  stream_driver<FAST, RESIDENT, RING, LAYOUT>(p, tr, smem, body, round_end, pre);
-  if (kDefer && tr.rounds > 0) {
+  int64_t last_blk;
+  if constexpr (RESIDENT && FAST) {
+    __shared__ int next_blk;
+    last_blk = stream_driver_dynamic<RING, LAYOUT>(p, tr, smem, &next_blk, body_b, block_end, pre);
+  } else {
+    // fixed rounds: wave w takes block mb_lo + 8r + w in round r
+    auto blk_of = [&](int r) { return tr.mb_lo + (int64_t)r * kWaves + wave; };
+    auto body = [&](const u32x4_t (&cur)[8], const unsigned char* hbase, int sbc, int r, int t) {
+      body_b(cur, hbase, sbc, r > 0 ? blk_of(r - 1) : (int64_t)-1, t);
+    };
+    auto round_end = [&](int r) { block_end(blk_of(r), r > 0 ? blk_of(r - 1) : (int64_t)-1); };
+    stream_driver<FAST, RESIDENT, RING, LAYOUT>(p, tr, smem, body, round_end, pre);
+    last_blk = tr.rounds > 0 ? blk_of(tr.rounds - 1) : (int64_t)-1;
+  }
+  if (kDefer && last_blk >= 0) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) finish_nb(tr.rounds - 1, nb);
+    for (int nb = 0; nb < NB; ++nb) finish_nb(last_blk, nb);
   }
   if (EPI == EPI_STORE) return;
 
