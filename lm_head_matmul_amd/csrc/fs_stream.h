@@ -534,7 +534,13 @@ __device__ __forceinline__ int64_t stream_driver_dynamic(const StreamParams& p, 
   if (!any) cur = tr.mb_hi - 1;  // loads of a wave without blocks stay in the tile; none is used
   int64_t nxt = -1;               // the block after the current one, -1 if none
   int64_t lb = cur;               // next position to load
-  int lsb = 0;
+  int lsb = 0;                    // position within the block
+  // The kernel with noise in its epilogue takes each block's sub-blocks in an
+  // order rotated per workgroup when rows have at most 8 of them (measured on
+  // MI355X: small decode B=32 118.7 -> 110.6 us; at 16 sub-blocks, and in the
+  // noise-table kernel, the rotation was slower).
+  const int rot = (LAYOUT == kLayoutEpilogue && nsub <= 8) ? (int)(blockIdx.x % (unsigned)nsub) : 0;
+  auto sb_at = [&](int j) { return j + rot < nsub ? j + rot : j + rot - nsub; };
   auto advance = [&]() {
     if (++lsb == nsub) {
       if (nxt >= 0) {
@@ -550,7 +556,7 @@ __device__ __forceinline__ int64_t stream_driver_dynamic(const StreamParams& p, 
   u32x4_t buf[U][8];
 #pragma unroll
   for (int k = 0; k < U - 1; ++k) {
-    load(buf[k], lb, lsb);
+    load(buf[k], lb, sb_at(lsb));
     advance();
   }
   pre();
@@ -568,11 +574,11 @@ __device__ __forceinline__ int64_t stream_driver_dynamic(const StreamParams& p, 
     for (int g = 0; g < ngrp; ++g) {
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        load(buf[(k + U - 1) % U], lb, lsb);
+        load(buf[(k + U - 1) % U], lb, sb_at(lsb));
         advance();
         // keep the loads above ahead of the compute below
         __builtin_amdgcn_sched_barrier(0);
-        body(buf[k], smem, g * U + k, pblk, g * U + k);
+        body(buf[k], smem, sb_at(g * U + k), pblk, g * U + k);
       }
     }
     block_end(cur, pblk);
@@ -1011,12 +1017,19 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
       *(u32x4_t*)(smem + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t*)(smem + bufbytes + row * rs + q * 16) = u32x4_t{0u, 0u, 0u, 0u};
     }
-    h_chunk_dma<2 * NB>(p, 0, smem);
+    // Each workgroup takes the chunks in a rotated order (from chunk blockIdx mod
+    // nchunk), so that workgroups stream different k ranges of their W rows and
+    // copy different H chunks at any one time.  In the same order for every
+    // workgroup, small decode (d=2048) at B=64 took 140 us instead of 115 on
+    // MI355X.  The masked kernels keep the plain order: the masked workload
+    // (d=5120, B=32) was 1% slower rotated.
+    const int rot = MASKED ? 0 : (int)(blockIdx.x % (unsigned)nchunk);
+    h_chunk_dma<2 * NB>(p, rot, smem);
     int64_t rowp[RM];  // the wave's block in each round of the pass
 #pragma unroll
     for (int r = 0; r < RM; ++r) rowp[r] = blk(0, r);
     u32x4_t buf[2][8];
-    load(buf[0], rowp[0], 0);
+    load(buf[0], rowp[0], rot * 2);
     // the first W item is in flight behind the chunk-0 copies: once at most its
     // 8 loads remain (vmcnt 8), this wave's copies have landed
     __builtin_amdgcn_sched_barrier(0);
@@ -1030,13 +1043,14 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
       // the next chunk.  Both paths leave the same 8 loads in flight into the
       // same registers, so the wait counts agree where they join.
       const bool last_on = nown >= (int64_t)(pass + 1) * RM;
-      for (int c = 0; c < nchunk; ++c) {
+      for (int cpos = 0; cpos < nchunk; ++cpos) {
+        const int c = cpos + rot < nchunk ? cpos + rot : cpos + rot - nchunk;  // this chunk
         const unsigned char* hb = smem + (cc & 1) * bufbytes;
         const int nc = c + 1 < nchunk ? c + 1 : 0;  // the chunk staged next
-        const bool last_c = c + 1 == nchunk;
+        const bool last_c = cpos + 1 == nchunk;     // the pass's k reduction completes here
         const int np = last_c && pass + 1 < npass ? pass + 1 : pass;
         const int64_t next_row = last_c ? blk(np, 0) : rowp[0];  // first item of the next chunk
-        const int next_sb = last_c ? 0 : (c + 1) * 2;
+        const int next_sb = last_c ? rot * 2 : nc * 2;
         // In the last chunk each round is finished right after its compute.  The
         // finish is long ALU work, so the second sub-block of the next round is
         // loaded into the buffer just freed before it: two items stay in flight
