@@ -912,7 +912,11 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     const int64_t npass = (rounds + cap - 1) / cap;
     cfg.rm = (int)((rounds + npass - 1) / npass);
   }
-  if (!cfg.dot && cfg.fast && cfg.rm == 0 && epi != EPI_STORE) {
+  // The tile's noise table, for rows of more than 8 sub-blocks (d > 2048).  At
+  // d <= 2048 the kernel running Philox in its epilogue, with its sub-blocks
+  // rotated per workgroup, measured faster on MI355X (small decode B=1..16:
+  // 118 -> 108 us); at d=4096 the table kernel is faster (195 vs 204 us).
+  if (!cfg.dot && cfg.fast && cfg.rm == 0 && epi != EPI_STORE && p.nsub > 8) {
     const int pitch = (int)tile_rows + 4;
     const int64_t nbytes = (int64_t)p.B * pitch * 4;
     if (total + nbytes <= kLdsMax) {

@@ -183,6 +183,8 @@ RAGGED = [
     (2, 512, 333, 1.3, 1), (7, 512, 333, 1.3, 0), (8, 512, 2000, 1.0, 0), (17, 256, 2000, 0.9, 0), (33, 520, 1234, 1.0, 0),
     (48, 768, 3001, 0.7, 0), (64, 2056, 1500, 1.0, 0), (65, 256, 999, 1.0, 0), (100, 264, 777, 0.8, 0),
     (2, 86016, 300, 1.0, 1), (2, 16, 7, 1.0, 0), (16, 20480, 300, 1.0, 2),
+    # rows of more than 8 sub-blocks with H resident: the kernel with the tile's noise table
+    (5, 3072, 3001, 0.8, 0), (16, 2560, 2049, 1.0, 0), (1, 4096, 5000, 1.0, 0),
 ]
 
 
