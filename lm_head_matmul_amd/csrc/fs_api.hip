@@ -91,7 +91,7 @@ int pow2_at_least(int x) {
   return p;
 }
 
-// Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB).
+// Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB, or <= kWideMaxB for the wide kernel).
 int choose_config(int B, int path, fsk::StreamConfig& cfg) {
   // AUTO takes the MFMA kernel at every batch size: on gfx950 it streams W
   // faster than the dot-product kernel even at B = 1 (measured).
@@ -107,7 +107,7 @@ int choose_config(int B, int path, fsk::StreamConfig& cfg) {
   }
   cfg.dot = dot;
   cfg.bd = dot ? pow2_at_least(B) : 0;
-  cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : 4);
+  cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : B <= fsk::kMfmaMaxB ? 4 : 8);
   cfg.fast = false;
   cfg.rm = 0;
   cfg.lds_bytes = 0;
@@ -176,9 +176,14 @@ void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int
 // starts at virtual row r0; `max_rows` bounds a chunk by the context's workspace.
 template <typename F>
 int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk,
-                      int max_rows = fsk::kMfmaMaxB) {
+                      int max_rows = fsk::kMfmaMaxB, bool wide = false) {
   const int B = base.B;
   int chunk = fsk::kMfmaMaxB < max_rows ? fsk::kMfmaMaxB : max_rows;
+  // more than kMfmaMaxB rows of the plain sampler: chunks of kWideMaxB rows for
+  // the wide kernel, which streams W once per chunk
+  if (wide && B > fsk::kMfmaMaxB && max_rows >= fsk::kWideMaxB && path != FS_PATH_DOT && !base.mask &&
+      base.samples <= 1 && base.d % 256 == 0 && epi == fsk::EPI_FLAT)
+    chunk = fsk::kWideMaxB;
   if (base.mask) {
     const int64_t rows = fsk::kMaskLdsMax / (4 * fsk::tile_mask_words(base.n_mblocks, base.n_tiles));
     if (rows < 1) return fail(FS_ERR_UNSUPPORTED, "V=%lld: a tile's mask does not fit the LDS staging area", (long long)base.V);
@@ -410,11 +415,14 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
   }
   fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
   const int nt = p.n_tiles;
-  return run_stream_chunks(p, path, fsk::EPI_FLAT, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
-    c.out_idx = out_idx + r0;
-    c.dbg_max = tile_max ? tile_max + (int64_t)r0 * nt : nullptr;
-    c.dbg_arg = tile_arg ? tile_arg + (int64_t)r0 * nt : nullptr;
-  });
+  return run_stream_chunks(
+      p, path, fsk::EPI_FLAT, (hipStream_t)stream,
+      [&](fsk::StreamParams& c, int r0) {
+        c.out_idx = out_idx + r0;
+        c.dbg_max = tile_max ? tile_max + (int64_t)r0 * nt : nullptr;
+        c.dbg_arg = tile_arg ? tile_arg + (int64_t)r0 * nt : nullptr;
+      },
+      fsk::kWideMaxB, true);
 }
 
 int fs_fmms_sample_multi(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,

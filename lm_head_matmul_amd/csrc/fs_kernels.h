@@ -143,6 +143,8 @@ constexpr int kDotMaxB = 2;
 constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
 constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
+constexpr int kWideMaxB = 128;      // batch chunk of the wide chunk-outer kernel (plain sampler, no mask)
+constexpr int kWideRowBytes = 528;  // its H rows: one 256-wide sub-block + 16 bytes against LDS bank conflicts
 // Which 16 bytes of a row's 512-byte sub-block lane group g (0..3) loads with
 // its load instruction e (0..7), and so which 8-value k chunk it feeds to MFMA
 // step e (H is read with the same map): lane_base(g) + e * lane_step bytes.

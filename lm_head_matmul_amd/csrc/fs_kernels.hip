@@ -839,6 +839,25 @@ __global__ void debug_gumbel_scan_init(unsigned long long* stats) {
 // else k-chunks (double-buffered when two fit); the tile's mask words are
 // staged when they fit beside H.  Prefers the layouts the fast driver takes.
 bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
+  if (!cfg.dot && cfg.nb == 8) {
+    // the wide chunk-outer kernel: fixed layout; the plain sampling epilogue,
+    // no mask, one sample per row, whole 256-wide sub-blocks
+    if (epi != EPI_FLAT || p.mask || p.samples > 1 || p.d % 256 != 0 || p.B > kWideMaxB) return false;
+    p.h_rows = kWideMaxB + 1;
+    p.h_rowstride = kWideRowBytes;
+    p.nsub = p.d / 256;
+    p.cs = 1;
+    p.nchunk = p.nsub;
+    p.nbuf = 2;
+    p.mask_words = 0;
+    p.mask_lds_off = 0;
+    p.noise_pitch = 0;
+    p.noise_lds_off = 0;
+    cfg.fast = true;
+    cfg.rm = 2;
+    cfg.lds_bytes = 2 * (kWideMaxB + 1) * kWideRowBytes;  // also covers the final reduction's scratch
+    return cfg.lds_bytes <= kLdsMax;
+  }
   const int Bp = cfg.dot ? cfg.bd : cfg.nb * 16;
   const int hr = cfg.dot ? cfg.bd : (p.B < Bp ? p.B + 1 : Bp);
   p.h_rows = hr;

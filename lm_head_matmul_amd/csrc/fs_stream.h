@@ -1116,6 +1116,188 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
 }
 
 // ---------------------------------------------------------------------------
+// Wide chunk-outer kernel: 128 batch columns (NB = 8) in one pass over W, for
+// batch chunks of 65 .. 128 rows of the plain sampler.  It streams W once per
+// 128 rows instead of once per 64.  H comes in chunks of one 256-wide
+// sub-block: rows padded to kWideRowBytes, row kWideMaxB the zero row the
+// padding lanes read, double-buffered (2 x 129 x 528 B = 136 KB of LDS).  A
+// pass covers RM = 2 rounds (2 x 8 accumulator sets per wave).  In each chunk,
+// round r's item is consumed from register buffer r after the item that
+// follows it -- round 1's, or the next chunk's round 0 -- has been sent to the
+// other buffer.  The chunk order is rotated per workgroup, as in the
+// chunk-outer kernel.
+// ---------------------------------------------------------------------------
+// Sub-block sb of H rows 0 .. B-1 into buf as whole 1 KB runs of 16-byte
+// pieces (an LDS-direct load writes 64 consecutive pieces): piece j of the
+// buffer is piece j mod 33 of row j / 33, piece 32 of a row being its padding
+// (filled with a copy of piece 0).  Rows past B repeat row B - 1; the runs end
+// before the zero row.  Every wave issues the same fixed number of copies.
+__device__ __forceinline__ void h_sub_dma(const StreamParams& p, int sb, unsigned char* buf) {
+  constexpr int kPieces = kWideRowBytes / 16;                          // 33
+  constexpr int kRunsPerWave = ((kPieces * kWideMaxB + 63) / 64 + kWaves - 1) / kWaves;  // 9
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrun = (kPieces * p.B + 63) / 64;
+#pragma unroll
+  for (int k = 0; k < kRunsPerWave; ++k) {
+    const int r0 = wave + k * kWaves;
+    const int run = r0 < nrun ? r0 : nrun - 1;
+    const int piece = run * 64 + lane;
+    const int row = piece / kPieces, col = piece - row * kPieces;
+    const int srow = row < p.B ? row : p.B - 1;
+    const int scol = col < kPieces - 1 ? col : 0;
+    __builtin_amdgcn_global_load_lds((const void*)(p.H + (int64_t)srow * p.ldh + sb * 256 + scol * 8),
+                                     (__attribute__((address_space(3))) void*)(buf + run * 1024), 16, 0, 0);
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(kThreads) fmms_kwide_kernel(const StreamParams p) {
+  constexpr int NB = 8, RM = 2;
+  constexpr int LAYOUT = kLayoutKouter;
+  constexpr int bufbytes = (kWideMaxB + 1) * kWideRowBytes;
+  static_assert(NB * 16 == kWideMaxB, "one batch column per lane group row");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, grp = lane >> 4;
+  const TileRange tr = tile_range(p);
+  int hoff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = nb * 16 + l16;
+    hoff[nb] = lane_base<LAYOUT>(grp) + (row < p.B ? row : kWideMaxB) * kWideRowBytes;
+  }
+  float bv[NB], lm[NB], ls[NB];
+  int32_t bi[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    bv[nb] = -INFINITY;
+    bi[nb] = -1;
+    lm[nb] = -INFINITY;
+    ls[nb] = 0.0f;
+  }
+  f32x4_t acc[RM][NB];
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = p.nsub;  // one sub-block per chunk
+  const int npass = (tr.rounds + RM - 1) / RM;
+  auto blk = [&](int pass, int r) { return tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave; };
+  const WLane wl = w_lane<LAYOUT>(p, tr, l16, grp);
+  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) { w_load8<LAYOUT>(p, tr, wl, mb, sb, buf); };
+  // One item: the 8 k-steps of its sub-block against the 8 batch blocks, in two
+  // halves of 4 blocks (the W registers serve both; B operands for only 4
+  // blocks are held, one k-step ahead).
+  auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hb, f32x4_t (&a)[NB]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4_t h0[4], h1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h0[q] = *(const u32x4_t*)(hb + hoff[hf * 4 + q]);
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          h1[q] = *(const u32x4_t*)(hb + hoff[hf * 4 + q] + (j + 1) * lane_step<LAYOUT>());
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          a[hf * 4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
+                                                                  __builtin_bit_cast(bf16x8_t, h0[q]), a[hf * 4 + q],
+                                                                  0, 0, 0);
+        if (j + 2 < 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            h0[q] = *(const u32x4_t*)(hb + hoff[hf * 4 + q] + (j + 2) * lane_step<LAYOUT>());
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          a[hf * 4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j + 1]),
+                                                                  __builtin_bit_cast(bf16x8_t, h1[q]), a[hf * 4 + q],
+                                                                  0, 0, 0);
+      }
+    }
+  };
+  auto finish = [&](int pass, int r, f32x4_t (&a)[NB]) {
+    const int64_t mbg = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
+    if (mbg < tr.mb_hi) {
+      const int v0 = (int)(mbg * 16) + grp * 4;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = nb * 16 + l16;
+        if (b < p.B) {
+          const float a4[4] = {a[nb][0], a[nb][1], a[nb][2], a[nb][3]};
+          const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), b);
+          epilogue_quad<EPI>(p, v0, a4, g, 0xFu, bv[nb], bi[nb], lm[nb], ls[nb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one N-block's noise at a time (register pressure)
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) a[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  if (tr.rounds > 0) {
+    for (int i = tid; i < kWideRowBytes / 16; i += kThreads) {  // the zero row of both buffers
+      *(u32x4_t*)(smem + kWideMaxB * kWideRowBytes + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
+      *(u32x4_t*)(smem + bufbytes + kWideMaxB * kWideRowBytes + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    const int rot = (int)(blockIdx.x % (unsigned)nchunk);
+    h_sub_dma(p, rot, smem);
+    u32x4_t buf[2][8];
+    load(buf[0], blk(0, 0), rot);
+    // the first W item is in flight behind the chunk's copies: once at most its
+    // 8 loads remain (vmcnt 8), this wave's copies have landed
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xF78);
+    __syncthreads();
+    int cc = 0;
+    for (int pass = 0; pass < npass; ++pass) {
+      for (int cpos = 0; cpos < nchunk; ++cpos) {
+        const int c = cpos + rot < nchunk ? cpos + rot : cpos + rot - nchunk;
+        const int nc = c + 1 < nchunk ? c + 1 : 0;
+        const bool last_c = cpos + 1 == nchunk;  // the pass's k reduction completes here
+        const unsigned char* hb = smem + (cc & 1) * bufbytes;
+        // the item after this chunk's round 1: the next chunk's round 0, or the next pass's
+        const int64_t next_mb = last_c ? blk(pass + 1 < npass ? pass + 1 : pass, 0) : blk(pass, 0);
+        const int next_sb = last_c ? rot : nc;
+        load(buf[1], blk(pass, 1), c);
+        // the next chunk's H, also after the last one (unused then): a copy on
+        // one path only would leave the compiler unsure of the loads in flight
+        h_sub_dma(p, nc, smem + ((cc + 1) & 1) * bufbytes);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[0], hb, acc[0]);
+        if (last_c) {
+          __builtin_amdgcn_sched_barrier(0);
+          finish(pass, 0, acc[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        load(buf[0], next_mb, next_sb);
+        __builtin_amdgcn_sched_barrier(0);
+        // a pass's round 1 past the tile's last round (odd round counts) is
+        // skipped by the whole workgroup; its load is left in place (it reads
+        // the tile's last block again) so that every chunk issues the same loads
+        if (pass * RM + 1 < tr.rounds) compute(buf[1], hb, acc[1]);
+        if (last_c) {
+          __builtin_amdgcn_sched_barrier(0);
+          finish(pass, 1, acc[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the chunk's copies were issued before the last W item (8 loads)
+        __builtin_amdgcn_s_waitcnt(0xF78);
+        __syncthreads();
+        ++cc;
+      }
+    }
+  }
+  finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
+}
+
+// ---------------------------------------------------------------------------
 // Dot-product streaming kernel for small batches (B <= BD <= 2): the same W
 // stream, with bf16 pair dot products on the vector ALU against H rows read
 // from LDS (one address per 16-lane group, i.e. broadcast reads).  The four
@@ -1321,6 +1503,10 @@ static hipError_t launch_kouter(const StreamParams& p, const StreamConfig& c, hi
 template <int EPI, bool MK>
 static hipError_t launch_masking(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
   const bool res = p.nchunk == 1;
+  if (c.nb == 8) {
+    if constexpr (!MK && EPI == EPI_FLAT) return launch_with_lds(fmms_kwide_kernel<EPI>, p.n_tiles, c.lds_bytes, s, p);
+    return hipErrorInvalidValue;
+  }
   if (c.rm > 0 && !c.dot) {
     switch (c.nb) {
       case 1: return launch_kouter<EPI, MK, 1>(p, c, s);
