@@ -185,6 +185,8 @@ RAGGED = [
     (2, 86016, 300, 1.0, 1), (2, 16, 7, 1.0, 0), (16, 20480, 300, 1.0, 2),
     # rows of more than 8 sub-blocks with H resident: the kernel with the tile's noise table
     (5, 3072, 3001, 0.8, 0), (16, 2560, 2049, 1.0, 0), (1, 4096, 5000, 1.0, 0),
+    # the wide kernel's 128-row chunks: two of them and a tail, a chunk of one row after it
+    (200, 512, 3001, 0.9, 0), (129, 256, 1500, 1.0, 0), (128, 2048, 4099, 0.7, 0),
 ]
 
 
@@ -387,3 +389,22 @@ def test_group_summaries_match_group_by_group_calls(fs, ctx):
     assert np.allclose(a[1], b[1], rtol=1e-5, atol=1e-5)
     diff = a[2] != b[2]
     assert diff.mean() <= 1e-3 + 1e-9 or np.all(np.abs(a[1][diff] - b[1][diff]) < 1e-3 * (1 + np.abs(b[1][diff])))
+
+
+@pytest.mark.parametrize("B,d,V", [(100, 512, 3001), (128, 1024, 5000)])
+def test_tile_maxima_wide(fs, ctx, B, d, V):
+    # per-tile maximizers of the wide kernel (128-row chunks) against the oracle's
+    import torch
+
+    H = synth.normal_bf16(B, d, seed=300 + B)
+    W = synth.normal_bf16(V, d, seed=301, std=2.0 / math.sqrt(d))
+    L = oracle.logits(H, W)
+    nt, bounds = fs.fs_fmms_tiling(ctx, B, d, V, 0)
+    say(f"tile maxima wide B={B} d={d} V={V} n_tiles={nt}")
+    tmax = torch.empty((B, nt), dtype=torch.float32, device="cuda")
+    targ = torch.empty((B, nt), dtype=torch.int32, device="cuda")
+    fs.fs_fmms_sample(ctx, dev_bf16(H), dev_bf16(W), 0.8, 5, 3, tile_max=tmax, tile_arg=targ)
+    _sync()
+    omax, oarg = oracle.tile_maxima(L, 0.8, 5, 3, np.array(bounds))
+    p_rows = [oracle.perturbed_row(L[b], 0.8, 5, 3, b) for b in range(B)]
+    check_tiles(tmax.cpu().numpy(), targ.cpu().numpy(), omax, oarg, p_rows, bounds, f"wide tiles B={B}")
