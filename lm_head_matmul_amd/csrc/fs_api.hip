@@ -168,8 +168,9 @@ void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int
 }
 
 // Launches the streaming kernel over the batch in chunks of at most
-// kMfmaMaxB rows (each chunk streams W once); with a mask, chunks are also
-// small enough for their tile masks to fit the LDS staging area.  `per_chunk`
+// kMfmaMaxB rows, or kWideMaxB rows for the wide kernel when `wide` allows it
+// (each chunk streams W once); with a mask, chunks are also small enough for
+// their tile masks to fit the LDS staging area.  `per_chunk`
 // adjusts the output pointers of a chunk that starts at batch row r0.
 // With base.samples > 1, base.B counts the call's virtual rows (row h, sample
 // s at h * samples + s): H and row_offset stay those of the call and each chunk
