@@ -224,17 +224,27 @@ __device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], c
   }
 }
 
+// One LDS-direct copy of 16 bytes per lane: the wave's 64 lanes fill the 1 KB
+// from lds (lane i at lds + 16 i).  It is written in inline assembly so that
+// the compiler leaves it out of its count of loads in flight.  With the
+// builtin, the next use of any load issued before a copy waited for every load
+// in flight (vmcnt 0), which drained the W prefetch once per H chunk.  The
+// compiler's own waits for W stay correct: a copy it does not count can only
+// make them wait longer.  The kernels order the copies themselves by explicit
+// waits before the barrier that hands a chunk to its readers.
+__device__ __forceinline__ void lds_copy16(const void* src, unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
 // Stage H chunk `cidx` (two 256-wide sub-blocks: 1 KB per row) straight from
 // global memory into LDS, without registers: one wave instruction moves one row
-// (lane l carries bytes [16 l, 16 l + 16) of it).  Rows b < B only (wave
+// (lane l carries bytes [16 l, 16 l + 16) of it).  Rows b < B (wave
 // b % kWaves issues row b); the zero row is written once at kernel start.  The
-// loads retire in order with the W loads of the issuing wave.
-// The copies are a fixed, fully unrolled sequence of ROWS rows per wave (row b
-// of wave w is w + 8k), every one issued: rows past B repeat row B - 1, which
-// writes the same bytes to the same place.  A loop over b < B would leave the
-// compiler unable to count the loads in flight after it, and the next use of
-// any earlier load would then wait for all of them (vmcnt 0), draining the W
-// prefetch at every chunk; guarded copies leave branches that do the same.
+// loads retire in order with the W loads of the issuing wave.  The copies are
+// a fixed, fully unrolled sequence of ROWS rows per wave (row b of wave w is
+// w + 8k) with no branches: rows past B repeat row B - 1, which writes the
+// same bytes to the same place.
 template <int ROWS>
 __device__ __forceinline__ void h_chunk_dma(const StreamParams& p, int cidx, unsigned char* buf) {
   const int lane = threadIdx.x & 63;
@@ -244,8 +254,7 @@ __device__ __forceinline__ void h_chunk_dma(const StreamParams& p, int cidx, uns
   for (int k = 0; k < ROWS; ++k) {
     const int b0 = wave + k * kWaves;
     const int b = b0 < p.B ? b0 : p.B - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)vrow_of(p, b).h * p.ldh),
-                                     (__attribute__((address_space(3))) void*)(buf + b * p.h_rowstride), 16, 0, 0);
+    lds_copy16(src + (int64_t)vrow_of(p, b).h * p.ldh, buf + b * p.h_rowstride);
   }
 }
 
@@ -1146,8 +1155,7 @@ __device__ __forceinline__ void h_sub_dma(const StreamParams& p, int sb, unsigne
     const int row = piece / kPieces, col = piece - row * kPieces;
     const int srow = row < p.B ? row : p.B - 1;
     const int scol = col < kPieces - 1 ? col : 0;
-    __builtin_amdgcn_global_load_lds((const void*)(p.H + (int64_t)srow * p.ldh + sb * 256 + scol * 8),
-                                     (__attribute__((address_space(3))) void*)(buf + run * 1024), 16, 0, 0);
+    lds_copy16(p.H + (int64_t)srow * p.ldh + sb * 256 + scol * 8, buf + run * 1024);
   }
 }
 
