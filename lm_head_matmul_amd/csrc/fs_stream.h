@@ -232,10 +232,16 @@ __device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], c
 // compiler's own waits for W stay correct: a copy it does not count can only
 // make them wait longer.  The kernels order the copies themselves by explicit
 // waits before the barrier that hands a chunk to its readers.
+// m0 (the LDS address) is reserved to the compiler, which does not track this
+// write to it.  That is safe only while no compiler-generated instruction in
+// these kernels uses m0; a CPU test checks that on the generated assembly.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(const void* src, unsigned char* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Stage H chunk `cidx` (two 256-wide sub-blocks: 1 KB per row) straight from
 // global memory into LDS, without registers: one wave instruction moves one row
