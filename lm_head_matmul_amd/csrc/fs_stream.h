@@ -52,10 +52,33 @@ __global__ void __launch_bounds__(kThreads)
   const int t0 = blockIdx.y * tpg;
   float v = -INFINITY, m = -INFINITY, s = 0.0f;
   int32_t i = -1;
-  for (int t = t0 + lane; t < t0 + tpg; t += 64) {
-    const int64_t o = (int64_t)b * n_tiles + t;
-    merge_best(v, i, ws_val[o], ws_idx[o]);
-    if (EPI == EPI_GROUP) lse_merge(m, s, ws_m[o], ws_s[o]);
+  // A lane's tiles in batches of kPer, every load of a batch issued before any
+  // merge: one memory round trip per batch (with a wait per tile, this launch
+  // took ~5 us at 256 tiles).  Slots past the end merge the neutral entry.
+  constexpr int kPer = 4;
+  const int64_t row = (int64_t)b * n_tiles;
+  for (int t1 = t0 + lane; t1 < t0 + tpg; t1 += 64 * kPer) {
+    float vv[kPer], mm[kPer], ss[kPer];
+    int32_t ii[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const bool ok = t1 + 64 * u < t0 + tpg;
+      const int64_t o = row + (ok ? t1 + 64 * u : t1);
+      const float lv = ws_val[o];
+      const int32_t li = ws_idx[o];
+      vv[u] = ok ? lv : -INFINITY;
+      ii[u] = ok ? li : -1;
+      if (EPI == EPI_GROUP) {
+        const float lm = ws_m[o], ls = ws_s[o];
+        mm[u] = ok ? lm : -INFINITY;
+        ss[u] = ok ? ls : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      merge_best(v, i, vv[u], ii[u]);
+      if (EPI == EPI_GROUP) lse_merge(m, s, mm[u], ss[u]);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -1074,6 +1097,15 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
           if (r == RM - 1 && RM > 1 && !last_on) break;
+          // Waves w and w + 4 share a SIMD, and the older one wins its issue
+          // arbitration: left alone, waves 0-3 finished each chunk ~8 us ahead
+          // of waves 4-7 and then idled at the chunk barrier (mid decode B=64,
+          // 23 us chunks).  The higher priority goes to the two in turn, round
+          // by round, so that both keep pace.
+          if (((r ^ (wave >> 2)) & 1) != 0)
+            __builtin_amdgcn_s_setprio(1);
+          else
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
           for (int sb = 0; sb < 2; ++sb) {
             // the W item after (r, sb): same round's next sub-block, the next
@@ -1284,6 +1316,12 @@ __global__ void __launch_bounds__(kThreads) fmms_kwide_kernel(const StreamParams
         // one path only would leave the compiler unsure of the loads in flight
         h_sub_dma(p, nc, smem + ((cc + 1) & 1) * bufbytes);
         __builtin_amdgcn_sched_barrier(0);
+        // waves w and w + 4 share a SIMD: the higher priority alternates between
+        // them round by round (as in the chunk-outer kernel)
+        if ((wave >> 2) != 0)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
         compute(buf[0], hb, acc[0]);
         if (last_c) {
           __builtin_amdgcn_sched_barrier(0);
@@ -1295,6 +1333,10 @@ __global__ void __launch_bounds__(kThreads) fmms_kwide_kernel(const StreamParams
         // a pass's round 1 past the tile's last round (odd round counts) is
         // skipped by the whole workgroup; its load is left in place (it reads
         // the tile's last block again) so that every chunk issues the same loads
+        if ((wave >> 2) != 0)
+          __builtin_amdgcn_s_setprio(0);
+        else
+          __builtin_amdgcn_s_setprio(1);
         if (pass * RM + 1 < tr.rounds) compute(buf[1], hb, acc[1]);
         if (last_c) {
           __builtin_amdgcn_sched_barrier(0);
