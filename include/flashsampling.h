@@ -82,9 +82,11 @@ void fs_destroy(fs_ctx* ctx);
 const char* fs_last_error(void);
 
 /* Number of vocabulary tiles (= workgroups) and the tile bounds used by
- * fs_fmms_sample for these sizes.  bounds, if not NULL, receives n_tiles + 1
- * ascending vocab ids: tile i covers [bounds[i], bounds[i+1]).  Tiles are
- * contiguous and balanced in units of 16 vocab rows. */
+ * fs_fmms_sample for these sizes when it reports tile maxima.  bounds, if not
+ * NULL, receives n_tiles + 1 ascending vocab ids: tile i covers
+ * [bounds[i], bounds[i+1]).  Tiles are contiguous and balanced in units of 16
+ * vocab rows.  Calls that do not report tile maxima may size the tiles per
+ * XCD instead (the sampled ids do not depend on the tiling). */
 int fs_fmms_tiling(fs_ctx* ctx, int B, int d, int64_t V, int path, int64_t* n_tiles, int64_t* bounds);
 
 /* Fused LM-head matmul + sample (FMMS).

@@ -422,6 +422,10 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
         c.out_idx = out_idx + r0;
         c.dbg_max = tile_max ? tile_max + (int64_t)r0 * nt : nullptr;
         c.dbg_arg = tile_arg ? tile_arg + (int64_t)r0 * nt : nullptr;
+        // tile maxima are reported over the tiling of fs_fmms_tiling; without
+        // them the planner may weight the tiles per XCD (the sample does not
+        // depend on the tiling)
+        c.tile_ratio = tile_max ? 0 : fsk::kXcdTileRatio;
       },
       fsk::kWideMaxB, true);
 }
@@ -442,7 +446,11 @@ int fs_fmms_sample_multi(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t l
   fill_common(p, ctx, H, ldh, W, ldw, B * num_samples, d, V, temperature, seed, step, mask, ldm);
   p.samples = num_samples;
   return run_stream_chunks(
-      p, path, fsk::EPI_FLAT, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) { c.out_idx = out_idx + r0; },
+      p, path, fsk::EPI_FLAT, (hipStream_t)stream,
+      [&](fsk::StreamParams& c, int r0) {
+        c.out_idx = out_idx + r0;
+        c.tile_ratio = fsk::kXcdTileRatio;
+      },
       ctx->max_B);
 }
 

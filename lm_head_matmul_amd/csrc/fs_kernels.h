@@ -64,6 +64,7 @@ struct StreamParams {
   int32_t* dbg_arg;
   float* logits;  // EPI_STORE: [B][ldl] fp32
   int64_t ldl;
+  int tile_ratio;  // 0: equal tiles; else XCD-weighted tiles (see tile_lo)
 };
 
 struct SampleParams {  // unfused second pass: sample from stored logits
@@ -167,6 +168,19 @@ constexpr int kouter_max_rounds(int epi, int nb, bool masked) {
   return (nb <= 2 || epi == EPI_STORE || (epi == EPI_FLAT && !masked)) ? 5 : 3;
 }
 constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
+
+// First 16-row block of tile t of n_tiles over n_mblocks blocks.  ratio == 0:
+// equal tiles.  ratio > 0: a tile of even index takes ratio / 1000 times the
+// blocks of an odd one.  Workgroup t runs on XCD t mod 8, and on MI355X the odd
+// XCDs streamed 2.6% slower than the even ones (mid decode B=64, two boxes):
+// their workgroups finished last.  Used for the chunk-outer kernel only (it
+// gained 1.5 us at mid decode B=32 and B=64, the resident kernel nothing).
+constexpr int kXcdTileRatio = 1026;
+__host__ __device__ inline int64_t tile_lo(int64_t t, int64_t n_mblocks, int n_tiles, int ratio) {
+  if (ratio == 0) return t * n_mblocks / n_tiles;
+  const auto w = [ratio](int64_t u) { return 1000 * (u / 2) + (int64_t)ratio * ((u + 1) / 2); };
+  return n_mblocks * w(t) / w(n_tiles);
+}
 constexpr int kTopkBins = 4096;    // first-level bins of the top-k radix select (key bits 31..20)
 constexpr int kTopkCap = 2048;     // boundary-bin ids the segment-parallel selection gathers per row
 constexpr int kTopkMaxSeg = 64;    // segments per row in the top-k launches

@@ -855,6 +855,7 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     p.noise_lds_off = 0;
     cfg.fast = true;
     cfg.rm = 2;
+    p.tile_ratio = 0;
     cfg.lds_bytes = 2 * (kWideMaxB + 1) * kWideRowBytes;  // also covers the final reduction's scratch
     return cfg.lds_bytes <= kLdsMax;
   }
@@ -924,13 +925,24 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   // up to kouter_max_rounds rounds.
   cfg.rm = 0;
   if (!cfg.dot && cfg.fast && p.nchunk > 1) {
-    const int64_t rounds = (tile_rows / 16 + kWaves - 1) / kWaves;
+    // XCD-weighted tiles where the caller allows them (tile_ratio set on entry):
+    // plain sampling without a mask, whole XCD pairs, at least 8 blocks a tile
+    if (p.tile_ratio != 0 && !(epi == EPI_FLAT && p.mask == nullptr && p.group_tiles == 0 && p.n_tiles % 8 == 0 &&
+                               p.n_mblocks >= 8 * (int64_t)p.n_tiles))
+      p.tile_ratio = 0;
+    int64_t max_blocks = 0;
+    for (int t = 0; t < p.n_tiles; ++t) {
+      const int64_t n = tile_lo(t + 1, p.n_mblocks, p.n_tiles, p.tile_ratio) - tile_lo(t, p.n_mblocks, p.n_tiles, p.tile_ratio);
+      if (n > max_blocks) max_blocks = n;
+    }
+    const int64_t rounds = (max_blocks + kWaves - 1) / kWaves;
     // passes of equal length: a short last pass would leave waves re-reading
     // their last block for the rounds they do not own
     const int cap = kouter_max_rounds(epi, cfg.nb, epi != EPI_STORE && p.mask != nullptr);
     const int64_t npass = (rounds + cap - 1) / cap;
     cfg.rm = (int)((rounds + npass - 1) / npass);
   }
+  if (cfg.rm == 0) p.tile_ratio = 0;
   // The tile's noise table, for rows of more than 8 sub-blocks (d > 2048).  At
   // d <= 2048 the kernel running Philox in its epilogue, with its sub-blocks
   // rotated per workgroup, measured faster on MI355X (small decode B=1..16:

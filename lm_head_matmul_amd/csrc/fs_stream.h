@@ -146,8 +146,8 @@ __device__ __forceinline__ TileRange tile_range(const StreamParams& p) {
     t.mb_lo = (int64_t)g * p.group_blocks + (int64_t)j * p.group_blocks / p.group_tiles;
     t.mb_hi = (int64_t)g * p.group_blocks + (int64_t)(j + 1) * p.group_blocks / p.group_tiles;
   } else {
-    t.mb_lo = (int64_t)blockIdx.x * p.n_mblocks / p.n_tiles;
-    t.mb_hi = (int64_t)(blockIdx.x + 1) * p.n_mblocks / p.n_tiles;
+    t.mb_lo = tile_lo(blockIdx.x, p.n_mblocks, p.n_tiles, p.tile_ratio);
+    t.mb_hi = tile_lo(blockIdx.x + 1, p.n_mblocks, p.n_tiles, p.tile_ratio);
   }
   t.rounds = (int)((t.mb_hi - t.mb_lo + kWaves - 1) / kWaves);
   return t;

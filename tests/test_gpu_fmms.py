@@ -203,6 +203,37 @@ def test_ragged_shapes_parity(fs, ctx, B, d, V, T, path):
     check_ids(gpu, ora, oracle_p_fn(L, rows, T, 42, 0), f"ragged {B}x{d}x{V}")
 
 
+# Chunk-outer shapes with at least 8 blocks of 16 vocab rows per tile: calls
+# without tile maxima run with XCD-weighted tiles, calls with them on the equal
+# tiling; both samples are checked against the oracle.
+XCD_TILED = [
+    # B, d, V, T
+    (24, 4096, 32771, 0.8), (64, 2048, 40003, 1.0), (40, 3072, 36000, 0.7),
+]
+
+
+@pytest.mark.parametrize("B,d,V,T", XCD_TILED)
+def test_xcd_weighted_tiles_parity(fs, ctx, B, d, V, T):
+    import torch
+
+    say(f"XCD-weighted tiles B={B} d={d} V={V} T={T}")
+    H = synth.normal_bf16(B, d, seed=300 + B)
+    W = synth.normal_bf16(V, d, seed=400 + B, std=2.0 / math.sqrt(d))
+    L = oracle.logits(H, W)
+    steps = 6
+    Hd, Wd = dev_bf16(H), dev_bf16(W)
+    gpu = _run_steps(fs, ctx, Hd, Wd, T, 9, range(steps))
+    rows = np.arange(B)
+    ora, _ = oracle.sample_rows_steps(L, rows, T, 9, 0, steps)
+    check_ids(gpu, ora, oracle_p_fn(L, rows, T, 9, 0), f"weighted tiles {B}x{d}x{V}")
+    nt, _ = fs.fs_fmms_tiling(ctx, B, d, V)
+    tmax = torch.empty((B, nt), dtype=torch.float32, device="cuda")
+    targ = torch.empty((B, nt), dtype=torch.int32, device="cuda")
+    eq = torch.stack([fs.fs_fmms_sample(ctx, Hd, Wd, T, 9, s, tile_max=tmax, tile_arg=targ) for s in range(steps)])
+    _sync()
+    check_ids(eq.cpu().numpy(), ora, oracle_p_fn(L, rows, T, 9, 0), f"equal tiles {B}x{d}x{V}")
+
+
 def test_strided_operands(fs, ctx):
     # ldh, ldw > d: row strides are honoured
     import torch
