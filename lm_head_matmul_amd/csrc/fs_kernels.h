@@ -174,7 +174,8 @@ constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
 // blocks of an odd one.  Workgroup t runs on XCD t mod 8, and on MI355X the odd
 // XCDs streamed 2.6% slower than the even ones (mid decode B=64, two boxes):
 // their workgroups finished last.  Used for the chunk-outer kernel only (it
-// gained 1.5 us at mid decode B=32 and B=64, the resident kernel nothing).
+// gained 1.0-1.3 us at mid decode B=24..64; the resident kernel and the group
+// summaries gained nothing).
 constexpr int kXcdTileRatio = 1026;
 __host__ __device__ inline int64_t tile_lo(int64_t t, int64_t n_mblocks, int n_tiles, int ratio) {
   if (ratio == 0) return t * n_mblocks / n_tiles;

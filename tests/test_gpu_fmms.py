@@ -203,12 +203,12 @@ def test_ragged_shapes_parity(fs, ctx, B, d, V, T, path):
     check_ids(gpu, ora, oracle_p_fn(L, rows, T, 42, 0), f"ragged {B}x{d}x{V}")
 
 
-# Chunk-outer shapes with at least 8 blocks of 16 vocab rows per tile: calls
+# Chunk-outer shapes with at least 16 blocks of 16 vocab rows per tile: calls
 # without tile maxima run with XCD-weighted tiles, calls with them on the equal
 # tiling; both samples are checked against the oracle.
 XCD_TILED = [
     # B, d, V, T
-    (24, 4096, 32771, 0.8), (64, 2048, 40003, 1.0), (40, 3072, 36000, 0.7),
+    (24, 4096, 65551, 0.8), (40, 2048, 70001, 1.0), (40, 3072, 66000, 0.7),
 ]
 
 
@@ -366,6 +366,7 @@ def test_grouped_summaries_and_combine(fs, ctx, B, d, G, n_groups, path):
     (64, 768, 1024, 4, 0),    # four batch blocks
     (3, 520, 48, 9, 0),       # groups not a multiple of 32 ids (offsets cross mask words)
     (5, 4096, 2000, 3, 2),    # chunked H, forced MFMA path
+    (24, 4096, 32768, 2, 0),  # chunk-outer kernel, 16 blocks a tile: XCD-weighted tiles in each group
 ])
 def test_group_summaries_in_one_launch(fs, ctx, B, d, G, n_groups, path):
     # fs_group_summaries over consecutive groups equals the oracle's per-group
