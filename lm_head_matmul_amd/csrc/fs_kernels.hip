@@ -877,7 +877,13 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     mask_bytes = (int)bytes;
   }
   const int budget = kLdsMax - mask_bytes;
-  if ((int64_t)hr * rowstride(p.nsub) <= budget) {  // whole H resident
+  // Whole H resident, except where rows have more than 8 sub-blocks and the
+  // tile's noise table would not fit beside it: the resident kernel then runs
+  // Philox in its epilogue, slower there than the chunk-outer kernel (mid
+  // decode B=15 and 16 on MI355X: 205.7 -> 202.1 us).  The stored-logits
+  // epilogue and the dot-product kernel use no table.
+  const bool table_fits = (int64_t)hr * rowstride(p.nsub) + (int64_t)p.B * (tile_rows + 4) * 4 <= budget;
+  if ((int64_t)hr * rowstride(p.nsub) <= budget && (p.nsub <= 8 || epi == EPI_STORE || cfg.dot || table_fits)) {
     p.cs = p.nsub;
     p.nchunk = 1;
     p.nbuf = 1;

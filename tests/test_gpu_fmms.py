@@ -209,6 +209,7 @@ def test_ragged_shapes_parity(fs, ctx, B, d, V, T, path):
 XCD_TILED = [
     # B, d, V, T
     (24, 4096, 65551, 0.8), (40, 2048, 70001, 1.0), (40, 3072, 66000, 0.7),
+    (16, 4096, 90007, 1.0),  # H would fit in LDS, its noise table beside it not: chunked H
 ]
 
 
