@@ -877,13 +877,15 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     mask_bytes = (int)bytes;
   }
   const int budget = kLdsMax - mask_bytes;
-  // Whole H resident, except where rows have more than 8 sub-blocks and the
-  // tile's noise table would not fit beside it: the resident kernel then runs
-  // Philox in its epilogue, slower there than the chunk-outer kernel (mid
-  // decode B=15 and 16 on MI355X: 205.7 -> 202.1 us).  The stored-logits
+  // Whole H resident where it fits, for the sampling epilogues only up to 16
+  // rows at d <= 2048 (small decode B=32 on MI355X: 109.7 us resident, 106.7
+  // chunk-outer) and at d > 2048 only if the tile's noise table fits beside it
+  // (without it the resident kernel runs Philox in its epilogue: mid decode
+  // B=15 and 16, 205.7 us, against 202.1 chunk-outer).  The stored-logits
   // epilogue and the dot-product kernel use no table.
   const bool table_fits = (int64_t)hr * rowstride(p.nsub) + (int64_t)p.B * (tile_rows + 4) * 4 <= budget;
-  if ((int64_t)hr * rowstride(p.nsub) <= budget && (p.nsub <= 8 || epi == EPI_STORE || cfg.dot || table_fits)) {
+  const bool prefer_resident = epi == EPI_STORE || cfg.dot || (p.nsub <= 8 ? p.B <= 16 : table_fits);
+  if ((int64_t)hr * rowstride(p.nsub) <= budget && prefer_resident) {
     p.cs = p.nsub;
     p.nchunk = 1;
     p.nbuf = 1;

@@ -187,6 +187,8 @@ RAGGED = [
     (5, 3072, 3001, 0.8, 0), (16, 2560, 2049, 1.0, 0), (1, 4096, 5000, 1.0, 0),
     # the wide kernel's 128-row chunks: two of them and a tail, a chunk of one row after it
     (200, 512, 3001, 0.9, 0), (129, 256, 1500, 1.0, 0), (128, 2048, 4099, 0.7, 0),
+    # more than 16 rows at d <= 2048: H in chunks although it would fit in LDS
+    (24, 2048, 3001, 0.9, 0), (32, 1024, 2000, 1.0, 0),
 ]
 
 
