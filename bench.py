@@ -194,7 +194,7 @@ def main():
         summarize_profiles(*args.summarize_profiles)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}),
+        print(json.dumps({"error": "the sampler runs on one GPU: --gpus must be 1", "n_gpus": args.gpus}),
               flush=True)
         sys.exit(2)
 
