@@ -44,7 +44,7 @@ extern "C" {
 enum {
   FS_OK = 0,
   FS_ERR_INVALID_ARG = -1, /* a pointer, size, stride or value is out of its documented range */
-  FS_ERR_UNSUPPORTED = -2, /* a combination this build does not implement */
+  FS_ERR_UNSUPPORTED = -2, /* a combination the library does not implement */
   FS_ERR_CAPACITY = -3,    /* a size exceeds what the context was created for */
   FS_ERR_HIP = -4          /* the HIP runtime reported an error (message in fs_last_error) */
 };
