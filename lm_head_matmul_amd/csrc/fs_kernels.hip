@@ -879,12 +879,14 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   const int budget = kLdsMax - mask_bytes;
   // Whole H resident where it fits, for the sampling epilogues only up to 16
   // rows at d <= 2048 (small decode B=32 on MI355X: 109.7 us resident, 106.7
-  // chunk-outer) and at d > 2048 only if the tile's noise table fits beside it
-  // (without it the resident kernel runs Philox in its epilogue: mid decode
-  // B=15 and 16, 205.7 us, against 202.1 chunk-outer).  The stored-logits
-  // epilogue and the dot-product kernel use no table.
+  // chunk-outer) and at d > 2048 only without a mask and if the tile's noise
+  // table fits beside it (without it the resident kernel runs Philox in its
+  // epilogue: mid decode B=15 and 16, 205.7 us, against 202.1 chunk-outer; with
+  // a mask, d=5120, B=1 and 8: 265.1 and 268.7 us, against 260.5 and 261.0).
+  // The stored-logits epilogue and the dot-product kernel use no table.
   const bool table_fits = (int64_t)hr * rowstride(p.nsub) + (int64_t)p.B * (tile_rows + 4) * 4 <= budget;
-  const bool prefer_resident = epi == EPI_STORE || cfg.dot || (p.nsub <= 8 ? p.B <= 16 : table_fits);
+  const bool prefer_resident =
+      epi == EPI_STORE || cfg.dot || (p.nsub <= 8 ? p.B <= 16 : table_fits && p.mask == nullptr);
   if ((int64_t)hr * rowstride(p.nsub) <= budget && prefer_resident) {
     p.cs = p.nsub;
     p.nchunk = 1;

@@ -257,21 +257,25 @@ def test_strided_operands(fs, ctx):
     assert torch.equal(a, b)
 
 
-def test_masked_parity_and_no_masked_picks(fs, ctx):
-    B, d, V, T = 12, 520, 3000, 1.0
+@pytest.mark.parametrize("B,d,V", [
+    (12, 520, 3000),
+    (6, 4096, 3001),  # rows of more than 8 sub-blocks with a mask: H in chunks, one batch block
+])
+def test_masked_parity_and_no_masked_picks(fs, ctx, B, d, V):
+    T = 1.0
     say(f"masked B={B} d={d} V={V}")
     H = synth.normal_bf16(B, d, seed=7)
     W = synth.outlier_bf16(V, d, 8, 9, 0.05, 0.5, 0.01)
     allowed = np.random.default_rng(10).random((B, V)) >= 0.3
     allowed[3] = False  # no allowed id: must sample -1
     allowed[4] = False
-    allowed[4, 2999] = True  # exactly one allowed id, in the ragged tail
+    allowed[4, V - 1] = True  # exactly one allowed id, in the ragged tail
     mask = synth.pack_mask(allowed)
     L = oracle.logits(H, W)
-    for path in (0, 1, 2) if B <= 8 else (0, 2):
+    for path in (0, 1, 2) if B <= 2 else (0, 2):
         gpu = _run_steps(fs, ctx, dev_bf16(H), dev_bf16(W), T, 5, range(30), mask=dev_words(mask), path=path)
         assert np.all(gpu[:, 3] == -1)
-        assert np.all(gpu[:, 4] == 2999)
+        assert np.all(gpu[:, 4] == V - 1)
         ok_rows = [b for b in range(B) if b != 3]
         for b in ok_rows:
             assert np.all(allowed[b, gpu[:, b]]), f"masked id drawn in row {b}"
