@@ -407,6 +407,7 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
       rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int q0) {
         c.logits = ctx->topk_ws + (int64_t)q0 * ctx->topk_ldl;
         c.ldl = ctx->topk_ldl;
+        c.tile_ratio = mask ? 0 : fsk::kXcdTileRatio;  // as the unfused call's store pass
       });
       if (rc != FS_OK) return rc;
       rc = launch_topk(ctx, ctx->topk_ws, ctx->topk_ldl, Bc, r0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
@@ -474,6 +475,8 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
     c.logits = logits_ws + (int64_t)r0 * ldl;
     c.ldl = ldl;
+    // the tiles of the fused call with the same mask: stored logits equal to its own bit for bit
+    c.tile_ratio = mask ? 0 : fsk::kXcdTileRatio;
   });
   if (rc != FS_OK) return rc;
   if (top_k > 0) return launch_topk(ctx, logits_ws, ldl, B, 0, V, temperature, seed, step, mask, ldm, top_k, out_idx, s);
@@ -516,6 +519,7 @@ int fs_softmax_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
     c.logits = logits_ws + (int64_t)r0 * ldl;
     c.ldl = ldl;
+    c.tile_ratio = fsk::kXcdTileRatio;  // the unmasked unfused call's tiles (this pass ignores the mask)
   });
   if (rc != FS_OK) return rc;
   fsk::CdfParams q;

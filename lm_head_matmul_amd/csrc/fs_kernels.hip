@@ -936,10 +936,12 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   cfg.rm = 0;
   if (!cfg.dot && cfg.fast && p.nchunk > 1) {
     // XCD-weighted tiles where the caller allows them (tile_ratio set on entry):
-    // plain sampling without a mask, whole XCD sets of tiles, at least 16
-    // blocks a tile (with fewer, one more block can add a round to a tile)
-    if (p.tile_ratio != 0 && !(epi == EPI_FLAT && p.mask == nullptr && p.group_tiles == 0 && p.n_tiles % 8 == 0 &&
-                               p.n_mblocks >= 16 * (int64_t)p.n_tiles))
+    // plain sampling without a mask or its stored-logits pass (the same tiles
+    // keep the stored logits equal bit for bit to the fused path's), whole XCD
+    // sets of tiles, at least 16 blocks a tile (with fewer, one more block can
+    // add a round to a tile)
+    if (p.tile_ratio != 0 && !((epi == EPI_FLAT || epi == EPI_STORE) && p.mask == nullptr && p.group_tiles == 0 &&
+                               p.n_tiles % 8 == 0 && p.n_mblocks >= 16 * (int64_t)p.n_tiles))
       p.tile_ratio = 0;
     int64_t max_blocks = 0;
     for (int t = 0; t < p.n_tiles; ++t) {

@@ -285,7 +285,8 @@ def test_masked_parity_and_no_masked_picks(fs, ctx, B, d, V):
 
 
 @pytest.mark.parametrize("B,d,V,path", [(2, 256, 4096, 1), (4, 256, 4096, 2), (40, 1024, 5000, 0),
-                                        (64, 2048, 3000, 2), (130, 264, 700, 0)])
+                                        (64, 2048, 3000, 2), (130, 264, 700, 0),
+                                        (24, 4096, 65551, 0)])  # XCD-weighted tiles without the mask
 def test_unfused_equals_fused(fs, ctx, B, d, V, path):
     import torch
 
