@@ -65,6 +65,7 @@ def _check_multi(fs, ctx, H, W, T, seed, step, S, mask=None, path=0, calls=2, la
     (20, 256, 2000, 5, 0),     # 100: two launches, row 12's samples split between them
     (1, 512, 1500, 2, 1),      # dot-product path
     (2, 768, 999, 33, 2),      # 66 virtual rows, forced MFMA path
+    (6, 4096, 65551, 4, 0),    # 24 virtual rows, chunk-outer kernel with XCD-weighted tiles
 ])
 def test_multi_sample_parity(fs, ctx, B, d, V, S, path):
     say(f"multi-sample B={B} d={d} V={V} S={S} path={path}")
