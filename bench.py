@@ -7,9 +7,12 @@ counter incrementing.  Headline: the mid-size decode head (d=4096, V=151936,
 B=64, T=0.7).  Prints ONE JSON line.
 
   value     achieved HBM GB/s = algorithmic bytes per step (V*d*2 + B*d*2 + B*4)
-            / measured time per step (HIP events on the launch stream)
-  roofline  that figure against MI355X's 8 TB/s; `traffic` is the measured
-            HBM bytes per launch from the committed rocprofv3 counter summary
+            / measured time per step (HIP events on the launch stream), after a
+            pre-run of at least 1 s that brings the GPU's clocks up
+  roofline  the streaming kernel alone: algorithmic bytes per launch / its mean
+            duration (HIP events recorded around each launch by the library's
+            timing hook) against MI355X's 8 TB/s; `traffic` is the measured HBM
+            bytes per launch from the committed rocprofv3 counter summary
   sweep     every B of the small and mid decode heads, the masked and grouped
             workloads, each next to the in-house unfused GEMM -> logits -> sample
   cpu_baseline  the CPU oracle timed on the host's cores on a bounded sample
@@ -54,6 +57,16 @@ def parse_args():
 
 def algorithmic_bytes(B, d, V, mask=False):
     return V * d * 2 + B * d * 2 + B * 4 + (B * ((V + 31) // 32) * 4 if mask else 0)
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def floors(B, d, V, mask=False):
+    """Lower bounds of a step's time: streaming its algorithmic bytes at peak HBM bandwidth,
+    and its 2 B V d multiply-adds at the dense bf16 MFMA peak."""
+    return {"hbm_floor_us": round(algorithmic_bytes(B, d, V, mask) / (PEAK_HBM_GBS * 1e3), 2),
+            "mfma_floor_us": round(2.0 * B * V * d / (PEAK_BF16_TFLOPS * 1e6), 2)}
 
 
 def kernel_source_hash():
@@ -187,6 +200,43 @@ class Timer:
         wall = time.perf_counter() - w0
         return e0.elapsed_time(e1) / n, wall  # ms per call, seconds
 
+    def run_with_kernel_events(self, fn, n, arm):
+        """Like run(), and each call's streaming kernel bracketed by its own pair of events
+        (arm(before, after) before the call): returns (ms per call, seconds, mean kernel ms)."""
+        t = self.torch
+        pairs = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in pairs:  # record once so that the HIP events exist before the library records them
+            a.record(self.stream)
+            b.record(self.stream)
+        t.cuda.synchronize()
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(self.stream)
+        for i in range(n):
+            arm(*pairs[i])
+            fn(i)
+        e1.record(self.stream)
+        t.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        kern = sum(a.elapsed_time(b) for a, b in pairs) / n
+        return e0.elapsed_time(e1) / n, wall, kern
+
+    def warm(self, fn, seconds, batch=50, tol=0.01):
+        """Runs fn until `seconds` have passed and two consecutive `batch`-call timings agree
+        within `tol` (at most 4 x `seconds`): the GPU's clocks ramp up over the first tens of
+        milliseconds of load after an idle spell.  Returns (calls, seconds)."""
+        w0 = time.perf_counter()
+        calls, prev = 0, None
+        while True:
+            ms, _ = self.run(lambda i: fn(calls + i), batch)
+            calls += batch
+            el = time.perf_counter() - w0
+            steady = prev is not None and abs(ms - prev) <= tol * prev
+            if (el >= seconds and steady) or el >= 4 * seconds:
+                return calls, el
+            prev = ms
+
 
 def main():
     args = parse_args()
@@ -227,7 +277,7 @@ def main():
     def H_for(name, B):
         return torch.from_numpy(synth.workload_H(name, B=B).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def time_fmms(name, B, steps, warmup, T, mask=None, unfused=False):
+    def time_fmms(name, B, steps, warmup, T, mask=None, unfused=False, warm_s=0.3):
         _, Ws = load_W(name)
         H = H_for(name, B)
         out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -242,6 +292,8 @@ def main():
             call(ctx, H, Ws[i % len(Ws)], T, 0, base + i, **kw)
 
         timer.run(lambda i: step(i, 0), warmup)
+        if warm_s > 0:  # clocks up after the W upload's idle spell
+            timer.warm(lambda i: step(i, 100000), warm_s)
         ms, wall = timer.run(lambda i: step(i, warmup), steps)
         return ms, wall
 
@@ -257,11 +309,39 @@ def main():
     # --- headline ---------------------------------------------------------------
     w = synth.WORKLOADS[args.workload]
     B, d, V, T = args.batch, w["d"], w["V"], w["T"]
-    log(f"headline {args.workload} B={B} d={d} V={V}: {args.warmup} warmup + {args.steps} timed steps")
-    ms, wall = time_fmms(args.workload, B, args.steps, args.warmup, T)
     algo = algorithmic_bytes(B, d, V)
+    _, Wsh = load_W(args.workload)
+    Hh = H_for(args.workload, B)
+    outh = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def hstep(i, base):
+        fs.fs_fmms_sample(ctx, Hh, Wsh[i % len(Wsh)], T, 0, base + i, out=outh)
+
+    log(f"headline {args.workload} B={B} d={d} V={V}: {args.warmup} warmup + {args.steps} timed steps")
+    # the driver's warmup, then the same K steps timed at once: what a fresh process sees
+    # while the GPU's clocks ramp up
+    timer.run(lambda i: hstep(i, 0), args.warmup)
+    cold_ms = None if args.profile else timer.run(lambda i: hstep(i, args.warmup), args.steps)[0]
+    # pre-run of the same call, outside the timed region: at least 1 s and until two
+    # consecutive 50-step batches agree within 1%
+    pre_calls, pre_s = timer.warm(lambda i: hstep(i, 10**6), 0.5 if args.profile else 1.0)
+    log(f"headline cold {cold_ms and cold_ms * 1e3} us/step; pre-run {pre_calls} steps in {pre_s:.2f}s")
+    # the timed region: exactly K steps
+    ms, wall = timer.run(lambda i: hstep(i, 2 * 10**6), args.steps)
     gbs = algo / (ms * 1e-3) / 1e9
-    log(f"headline: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of 8 TB/s), wall {wall:.3f}s")
+    # the streaming kernel's own duration: the next K steps with each launch between a pair
+    # of events recorded by the library (the extra event records cost the step ~7 us, so
+    # the step time above is taken without them)
+    _, _, kern_ms = timer.run_with_kernel_events(lambda i: hstep(i, 3 * 10**6), args.steps,
+                                                 lambda a, b: fs.fs_profile_next_launch(ctx, a, b))
+    kgbs = algo / (kern_ms * 1e-3) / 1e9
+    log(f"headline: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s, {gbs / PEAK_HBM_GBS:.1%} of 8 TB/s); streaming kernel "
+        f"{kern_ms * 1e3:.1f} us ({kgbs:.0f} GB/s, {kgbs / PEAK_HBM_GBS:.1%}); wall {wall:.3f}s")
+    # five more K-step runs (median), and single-step latency
+    reps, lat = [ms] * 5, [ms]
+    if not args.profile:
+        reps = sorted(timer.run(lambda i, r=r: hstep(i, (4 + r) * 10**6), args.steps)[0] for r in range(5))
+        lat = sorted(timer.run(lambda j, i=i: hstep(j, 9 * 10**6 + i), 1)[0] for i in range(20))
     if args.profile:
         ms_u = None
     else:
@@ -284,11 +364,22 @@ def main():
         "config": {"workload": f"{args.workload}_head", "B": B, "d": d, "V": V, "temperature": T, "top_k": 0,
                    "us_per_step": round(ms * 1e3, 2), "rows_per_s": round(B / (ms * 1e-3)),
                    "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                   "stream_kernel_us": round(kern_ms * 1e3, 2),
+                   "median_of_5_us_per_step": round(reps[2] * 1e3, 2),
+                   "single_step_latency_us_median": round(lat[len(lat) // 2] * 1e3, 2),
+                   "cold_us_per_step": None if cold_ms is None else round(cold_ms * 1e3, 2),
+                   "cold_note": "the same K steps right after the driver's warmup, before the pre-run: the "
+                                "GPU's clocks ramp up over the first ~100 ms of load",
+                   "prerun": {"steps": pre_calls, "seconds": round(pre_s, 3)},
                    "unfused_us_per_step": None if ms_u is None else round(ms_u * 1e3, 2),
                    "fused_speedup_vs_unfused": None if ms_u is None else round(ms_u / ms, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "algorithmic_bytes_per_launch": algo},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": algo,
+                     "kernel_us": round(kern_ms * 1e3, 2),
+                     "note": "achieved = algorithmic bytes of one launch / the streaming kernel's mean duration "
+                             "(HIP events around each launch, K steps right after the timed region); traffic = calibrated "
+                             "FETCH_SIZE + WRITE_SIZE per launch from profiles/ (null if the kernels changed)"},
         "context": "pages: up to 19% lower time per output token end to end in vLLM on NVIDIA "
                    "H100/H200/B200/B300 (not comparable; context only)",
     }
@@ -308,7 +399,7 @@ def main():
                               "GB_per_s": round(ab / (f_ms * 1e-3) / 1e9, 1),
                               "pct_peak": round(100 * ab / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                               "rows_per_s": round(b / (f_ms * 1e-3)), "unfused_us_per_step": round(u_ms * 1e3, 2),
-                              "speedup_vs_unfused": round(u_ms / f_ms, 3)})
+                              "speedup_vs_unfused": round(u_ms / f_ms, 3), **floors(b, ww["d"], ww["V"])})
                 log(f"sweep {sweep[-1]}")
             del weights[name]
             torch.cuda.empty_cache()
@@ -444,20 +535,35 @@ def main():
         Hh = synth.workload_H(args.workload, B=B)
         oracle.lib()
         cores = oracle.num_threads()
-        rows_done, t_used = 0, 0.0
-        t0 = time.perf_counter()
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+        except (OSError, StopIteration):
+            pass
+        # runs of r rows each, until the time budget or the step's rows are used up; the per-row
+        # cost is the median over runs (the oracle's cost is linear in the rows it samples)
         r = min(8, B)
-        while t_used < args.cpu_seconds and rows_done < B:
-            oracle.fmms_sample(Hh[rows_done:rows_done + r], Wh, T, 0, 0)
-            rows_done += r
+        per_row, rows_done, t_used = [], 0, 0.0
+        t0 = time.perf_counter()
+        while t_used < args.cpu_seconds and (rows_done < B or len(per_row) < 3):
+            r0 = rows_done % B
+            t1 = time.perf_counter()
+            oracle.fmms_sample(Hh[r0:r0 + r], Wh, T, 0, 0)
+            per_row.append((time.perf_counter() - t1) / len(Hh[r0:r0 + r]))
+            rows_done += len(Hh[r0:r0 + r])
             t_used = time.perf_counter() - t0
-        per_step = t_used / rows_done * B  # the oracle's cost is linear in the rows it samples
+        per_row.sort()
+        per_step = per_row[len(per_row) // 2] * B
         cpu_gbs = algo / per_step / 1e9
-        sample = (f"{rows_done} of the {B} rows of one step (full V={V}, d={d}: fp64 logits, noise, argmax) "
-                  f"in {t_used:.1f}s" + ("" if rows_done == B else f"; step time scaled by {B}/{rows_done}"))
+        sample = (f"{len(per_row)} runs of {r} rows of the headline step (full V={V}, d={d}: fp64 logits, noise, "
+                  f"argmax), {rows_done} rows in {t_used:.1f}s; step time = median per-row time x {B} rows")
         result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                                  "sample": sample, "seconds_per_step": round(per_step, 3),
-                                  "us_per_step": round(per_step * 1e6, 1)}
+                                  "sample": sample, "cpu_model": cpu_model, "runs": len(per_row),
+                                  "seconds_per_step": round(per_step, 3), "us_per_step": round(per_step * 1e6, 1),
+                                  "per_row_seconds_min_median_max": [round(per_row[0], 4),
+                                                                     round(per_row[len(per_row) // 2], 4),
+                                                                     round(per_row[-1], 4)]}
         log(f"cpu baseline {result['cpu_baseline']}")
 
     fs.fs_destroy(ctx)

@@ -201,6 +201,17 @@ int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh
 int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int n_groups, int B, uint64_t seed,
                      uint64_t step, int mode, int32_t* out_idx);
 
+/* Timing hook for measurement.  The next streaming call made on this context
+ * records `before` on its stream right before its streaming (LM-head) kernel
+ * and `after` right after it, ahead of the small tile reduction that
+ * follows, then forgets both; with several batch chunks, `before` precedes the
+ * first chunk's kernel and `after` follows the last one's.  Both are
+ * hipEvent_t handles passed as void*, created by the caller (with timing
+ * enabled) and owned by it; both NULL disarms.  The elapsed time between them
+ * is the streaming kernel's duration as seen on that stream.
+ * Returns FS_ERR_INVALID_ARG if exactly one of them is NULL. */
+int fs_profile_next_launch(fs_ctx* ctx, void* before, void* after);
+
 /* Test exports. */
 
 /* r_out[i] (if not NULL) = Philox word driving vocab id v0 + i of row `row` at

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     fs_group_summaries,
     fs_group_summary,
     fs_last_error,
+    fs_profile_next_launch,
     fs_softmax_sample,
     fs_unfused_sample,
     summary_views,

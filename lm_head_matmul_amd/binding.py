@@ -49,6 +49,7 @@ SIGNATURES = {
     "fs_group_summaries": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _I, _F, _U64, _U64, _P, _I64, _P,
                                 _I]),
     "fs_group_combine": (_I, [_P, _P, _P, _I, _I, _U64, _U64, _I, _P]),
+    "fs_profile_next_launch": (_I, [_P, _P, _P]),
     "fs_debug_philox": (_I, [_P, _P, _U64, _U64, _I, _I64, _I64, _P, _P]),
     "fs_debug_gumbel_bits": (_I, [_P, _P, _U64, _I64, _P]),
     "fs_debug_gumbel_scan": (_I, [_P, _P, _P]),
@@ -100,12 +101,38 @@ def _matrix(t: torch.Tensor, name: str) -> tuple[int, int, int]:
     return t.shape[0], t.shape[1], t.stride(0)
 
 
-def _mask_args(mask):
+def _mask_args(mask, B: int, V: int):
+    """Pointer and row stride of a packed [B, >= ceil(V/32)] mask (None: no mask)."""
     if mask is None:
         return None, 0
     if mask.dtype not in (torch.int32, torch.uint32) or mask.dim() != 2 or mask.stride(1) != 1:
         raise TypeError("mask must be a 2-D row-major int32/uint32 tensor of packed words")
+    if not mask.is_cuda:
+        raise ValueError("mask must live on the GPU")
+    if mask.shape[0] < B or mask.shape[1] < (V + 31) // 32:
+        raise ValueError(f"mask must be at least [{B}, {(V + 31) // 32}] words (got {tuple(mask.shape)})")
     return mask.data_ptr(), mask.stride(0)
+
+
+def _device_buffer(t: torch.Tensor, dtype, numel: int, name: str) -> None:
+    """A contiguous GPU tensor of `dtype` with room for `numel` elements."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+
+
+def _logits_ws(t: torch.Tensor, B: int, V: int) -> None:
+    if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1:
+        raise TypeError("logits_ws must be a 2-D row-major float32 tensor")
+    if not t.is_cuda:
+        raise ValueError("logits_ws must live on the GPU")
+    if t.shape[0] < B or t.shape[1] < V:
+        raise ValueError(f"logits_ws must be at least [{B}, {V}] (got {tuple(t.shape)})")
 
 
 # --- context ---------------------------------------------------------------
@@ -145,7 +172,14 @@ def fs_fmms_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: floa
         raise ValueError("H and W disagree on d")
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
-    mptr, ldm = _mask_args(mask)
+    _device_buffer(out, torch.int32, B, "out")
+    if (tile_max is None) != (tile_arg is None):
+        raise ValueError("tile_max and tile_arg go together")
+    if tile_max is not None:
+        nt, _ = fs_fmms_tiling(ctx, B, d, V, path)
+        _device_buffer(tile_max, torch.float32, B * nt, "tile_max")
+        _device_buffer(tile_arg, torch.int32, B * nt, "tile_arg")
+    mptr, ldm = _mask_args(mask, B, V)
     _check(_lib.fs_fmms_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(), _dptr(tile_max),
                                _dptr(tile_arg), path))
@@ -162,9 +196,8 @@ def fs_fmms_sample_multi(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature
         raise ValueError("H and W disagree on d")
     if out is None:
         out = torch.empty((B, num_samples), dtype=torch.int32, device=H.device)
-    if out.dtype != torch.int32 or not out.is_contiguous() or out.numel() != B * num_samples:
-        raise TypeError("out must be a contiguous int32 tensor of B * num_samples elements")
-    mptr, ldm = _mask_args(mask)
+    _device_buffer(out, torch.int32, B * num_samples, "out")
+    mptr, ldm = _mask_args(mask, B, V)
     _check(_lib.fs_fmms_sample_multi(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                      float(temperature), seed, step, mptr, ldm, num_samples, out.data_ptr(), path))
     return out
@@ -179,11 +212,11 @@ def fs_unfused_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: f
         raise ValueError("H and W disagree on d")
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
+    _device_buffer(out, torch.int32, B, "out")
     if logits_ws is None:
         logits_ws = torch.empty((B, (V + 3) // 4 * 4), dtype=torch.float32, device=H.device)
-    if logits_ws.dtype != torch.float32 or logits_ws.dim() != 2 or logits_ws.stride(1) != 1:
-        raise TypeError("logits_ws must be a 2-D row-major float32 tensor")
-    mptr, ldm = _mask_args(mask)
+    _logits_ws(logits_ws, B, V)
+    mptr, ldm = _mask_args(mask, B, V)
     _check(_lib.fs_unfused_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                   float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(),
                                   logits_ws.data_ptr(), logits_ws.stride(0), path))
@@ -200,11 +233,11 @@ def fs_softmax_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: f
         raise ValueError("H and W disagree on d")
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
+    _device_buffer(out, torch.int32, B, "out")
     if logits_ws is None:
         logits_ws = torch.empty((B, (V + 3) // 4 * 4), dtype=torch.float32, device=H.device)
-    if logits_ws.dtype != torch.float32 or logits_ws.dim() != 2 or logits_ws.stride(1) != 1:
-        raise TypeError("logits_ws must be a 2-D row-major float32 tensor")
-    mptr, ldm = _mask_args(mask)
+    _logits_ws(logits_ws, B, V)
+    mptr, ldm = _mask_args(mask, B, V)
     _check(_lib.fs_softmax_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                   float(temperature), seed, step, mptr, ldm, out.data_ptr(), logits_ws.data_ptr(),
                                   logits_ws.stride(0), path))
@@ -226,7 +259,8 @@ def fs_group_summary(ctx: int, H: torch.Tensor, W_group: torch.Tensor, vocab_off
         raise ValueError("H and W_group disagree on d")
     if out is None:
         out = torch.empty((B, 3), dtype=torch.int32, device=H.device)
-    mptr, ldm = _mask_args(mask)
+    _device_buffer(out, torch.int32, B * 3, "out")
+    mptr, ldm = _mask_args(mask, B, vocab_offset + G)
     _check(_lib.fs_group_summary(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W_group.data_ptr(), ldw, B, d,
                                  vocab_offset, G, float(temperature), seed, step, mptr, ldm, out.data_ptr(), path))
     return out
@@ -245,7 +279,8 @@ def fs_group_summaries(ctx: int, H: torch.Tensor, W: torch.Tensor, vocab_offset:
     n_groups = V // group_size
     if out is None:
         out = torch.empty((n_groups, B, 3), dtype=torch.int32, device=H.device)
-    mptr, ldm = _mask_args(mask)
+    _device_buffer(out, torch.int32, n_groups * B * 3, "out")
+    mptr, ldm = _mask_args(mask, B, vocab_offset + V)
     _check(_lib.fs_group_summaries(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, vocab_offset,
                                    group_size, n_groups, float(temperature), seed, step, mptr, ldm, out.data_ptr(),
                                    path))
@@ -258,11 +293,25 @@ def fs_group_combine(ctx: int, summaries: torch.Tensor, seed: int, step: int, mo
     if summaries.dtype != torch.int32 or summaries.dim() != 3 or summaries.shape[2] != 3 or not summaries.is_contiguous():
         raise TypeError("summaries must be a contiguous [n_groups, B, 3] int32 tensor")
     n_groups, B, _ = summaries.shape
+    if not summaries.is_cuda:
+        raise ValueError("summaries must live on the GPU")
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=summaries.device)
+    _device_buffer(out, torch.int32, B, "out")
     _check(_lib.fs_group_combine(ctx, _stream_ptr(stream), summaries.data_ptr(), n_groups, B, seed, step, mode,
                                  out.data_ptr()))
     return out
+
+
+# --- measurement -------------------------------------------------------------
+
+def fs_profile_next_launch(ctx: int, before=None, after=None) -> None:
+    """Arm the next streaming call to record torch.cuda.Event `before` / `after` around its
+    streaming kernel (both None disarms).  Events must have been recorded once already,
+    so that they exist as HIP events."""
+    b = None if before is None else before.cuda_event
+    a = None if after is None else after.cuda_event
+    _check(_lib.fs_profile_next_launch(ctx, b, a))
 
 
 # --- test exports -------------------------------------------------------------

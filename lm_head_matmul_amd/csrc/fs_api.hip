@@ -8,7 +8,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <string>
 
 #include "../../include/flashsampling.h"
 #include "fs_kernels.h"
@@ -41,19 +40,21 @@ struct fs_ctx {
   uint32_t* topk_arrive;
   // conventional comparator: [max_B][kCdfMaxSeg] segment max, sum of exp, sum of probabilities
   float* cdf_ws;
+  // timing hook (fs_profile_next_launch): events the next streaming call records
+  hipEvent_t prof_before;
+  hipEvent_t prof_after;
 };
 
 namespace {
 
-thread_local std::string g_error;
+// A fixed buffer: reporting an error allocates nothing.
+thread_local char g_error[512];
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
   va_end(ap);
-  g_error = buf;
   return code;
 }
 
@@ -175,10 +176,14 @@ void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int
 // With base.samples > 1, base.B counts the call's virtual rows (row h, sample
 // s at h * samples + s): H and row_offset stay those of the call and each chunk
 // starts at virtual row r0; `max_rows` bounds a chunk by the context's workspace.
+// Events armed by fs_profile_next_launch are recorded before the first chunk's
+// streaming kernel and after the last one's, then disarmed.
 template <typename F>
-int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk,
+int run_stream_chunks(fs_ctx* ctx, fsk::StreamParams base, int path, int epi, hipStream_t stream, F per_chunk,
                       int max_rows = fsk::kMfmaMaxB, bool wide = false) {
   const int B = base.B;
+  hipEvent_t ev_before = ctx->prof_before, ev_after = ctx->prof_after;
+  ctx->prof_before = ctx->prof_after = nullptr;
   int chunk = fsk::kMfmaMaxB < max_rows ? fsk::kMfmaMaxB : max_rows;
   // more than kMfmaMaxB rows of the plain sampler: chunks of kWideMaxB rows for
   // the wide kernel, which streams W once per chunk
@@ -206,7 +211,8 @@ int run_stream_chunks(fsk::StreamParams base, int path, int epi, hipStream_t str
     if (rc != FS_OK) return rc;
     if (!fsk::plan_stream(p, cfg, epi))
       return fail(FS_ERR_UNSUPPORTED, "shape B=%d d=%d does not fit the LDS budget", Bc, p.d);
-    hipError_t e = fsk::launch_stream(p, cfg, epi, stream);
+    const bool last = r0 + chunk >= B;
+    hipError_t e = fsk::launch_stream(p, cfg, epi, stream, r0 == 0 ? ev_before : nullptr, last ? ev_after : nullptr);
     if (e != hipSuccess) return hip_fail(e, "streaming kernel launch");
   }
   return FS_OK;
@@ -264,7 +270,7 @@ int launch_topk(const fs_ctx* ctx, const float* logits, int64_t ldl, int rows, i
 
 extern "C" {
 
-const char* fs_last_error(void) { return g_error.c_str(); }
+const char* fs_last_error(void) { return g_error; }
 
 int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k) {
   if (!out) return fail(FS_ERR_INVALID_ARG, "out is NULL");
@@ -404,7 +410,7 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
     for (int r0 = 0; r0 < B; r0 += ctx->topk_rows) {
       const int Bc = (B - r0) < ctx->topk_rows ? (B - r0) : ctx->topk_rows;
       fill_common(p, ctx, H + (int64_t)r0 * ldh, ldh, W, ldw, Bc, d, V, temperature, seed, step, nullptr, 0);
-      rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int q0) {
+      rc = run_stream_chunks(ctx, p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int q0) {
         c.logits = ctx->topk_ws + (int64_t)q0 * ctx->topk_ldl;
         c.ldl = ctx->topk_ldl;
         c.tile_ratio = mask ? 0 : fsk::kXcdTileRatio;  // as the unfused call's store pass
@@ -418,7 +424,7 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
   fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
   const int nt = p.n_tiles;
   return run_stream_chunks(
-      p, path, fsk::EPI_FLAT, (hipStream_t)stream,
+      ctx, p, path, fsk::EPI_FLAT, (hipStream_t)stream,
       [&](fsk::StreamParams& c, int r0) {
         c.out_idx = out_idx + r0;
         c.dbg_max = tile_max ? tile_max + (int64_t)r0 * nt : nullptr;
@@ -447,7 +453,7 @@ int fs_fmms_sample_multi(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t l
   fill_common(p, ctx, H, ldh, W, ldw, B * num_samples, d, V, temperature, seed, step, mask, ldm);
   p.samples = num_samples;
   return run_stream_chunks(
-      p, path, fsk::EPI_FLAT, (hipStream_t)stream,
+      ctx, p, path, fsk::EPI_FLAT, (hipStream_t)stream,
       [&](fsk::StreamParams& c, int r0) {
         c.out_idx = out_idx + r0;
         c.tile_ratio = fsk::kXcdTileRatio;
@@ -472,7 +478,7 @@ int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   hipStream_t s = (hipStream_t)stream;
   fsk::StreamParams p;
   fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, nullptr, 0);  // the GEMM pass ignores the mask
-  rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
+  rc = run_stream_chunks(ctx, p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
     c.logits = logits_ws + (int64_t)r0 * ldl;
     c.ldl = ldl;
     // the tiles of the fused call with the same mask: stored logits equal to its own bit for bit
@@ -516,7 +522,7 @@ int fs_softmax_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh,
   hipStream_t s = (hipStream_t)stream;
   fsk::StreamParams p;
   fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, nullptr, 0);
-  rc = run_stream_chunks(p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
+  rc = run_stream_chunks(ctx, p, path, fsk::EPI_STORE, s, [&](fsk::StreamParams& c, int r0) {
     c.logits = logits_ws + (int64_t)r0 * ldl;
     c.ldl = ldl;
     c.tile_ratio = fsk::kXcdTileRatio;  // the unmasked unfused call's tiles (this pass ignores the mask)
@@ -568,7 +574,7 @@ int fs_group_summary(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, 
   fsk::StreamParams p;
   fill_common(p, ctx, H, ldh, W_group, ldw, B, d, G, temperature, seed, step, mask, ldm);
   p.vocab_offset = vocab_offset;
-  return run_stream_chunks(p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
+  return run_stream_chunks(ctx, p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
     c.out_sum = reinterpret_cast<fsk::GroupSummary*>(out + r0);
   });
 }
@@ -604,7 +610,7 @@ int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh
     p.n_tiles = (int)(tpg * ng);
     p.n_mblocks = gblocks * ng;
     p.group_out_stride = B;
-    rc = run_stream_chunks(p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
+    rc = run_stream_chunks(ctx, p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
       c.out_sum = reinterpret_cast<fsk::GroupSummary*>(out + (int64_t)g0 * B + r0);
     });
     if (rc != FS_OK) return rc;
@@ -624,6 +630,14 @@ int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int
   hipError_t e = fsk::launch_group_combine(reinterpret_cast<const fsk::GroupSummary*>(s), n_groups, B, seed, step,
                                            mode, out_idx, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return FS_OK;
+}
+
+int fs_profile_next_launch(fs_ctx* ctx, void* before, void* after) {
+  if (!ctx) return fail(FS_ERR_INVALID_ARG, "ctx is NULL");
+  if ((before == nullptr) != (after == nullptr)) return fail(FS_ERR_INVALID_ARG, "before and after go together");
+  ctx->prof_before = (hipEvent_t)before;
+  ctx->prof_after = (hipEvent_t)after;
   return FS_OK;
 }
 

@@ -196,7 +196,10 @@ inline int64_t tile_mask_words(int64_t n_mblocks, int n_tiles) {
 // if the shape does not fit the kernels' LDS budget.
 bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi);
 
-hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream);
+// ev_before / ev_after (may be null): recorded on `stream` right before and
+// right after the streaming kernel (before the tile reduction), for timing.
+hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream,
+                         hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr);
 template <int EPI>
 hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& cfg, hipStream_t stream);
 hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream);

@@ -974,19 +974,23 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
 }
 
 // The streaming pass, then (sampling epilogues) the reduction over its tiles.
-hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream) {
+hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi, hipStream_t stream,
+                         hipEvent_t ev_before, hipEvent_t ev_after) {
   hipError_t e;
   const dim3 rgrid((p.B + kWaves - 1) / kWaves);
+  if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
   switch (epi) {
     case EPI_FLAT:
       e = launch_stream_epi<EPI_FLAT>(p, cfg, stream);
       if (e != hipSuccess) return e;
+      if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
       hipLaunchKernelGGL(reduce_tiles_kernel<EPI_FLAT>, rgrid, dim3(kThreads), 0, stream, p.B, p.n_tiles, p.ws_val,
                          p.ws_idx, nullptr, nullptr, p.out_idx, nullptr, p.n_tiles, (int64_t)0);
       return hipGetLastError();
     case EPI_GROUP:
       e = launch_stream_epi<EPI_GROUP>(p, cfg, stream);
       if (e != hipSuccess) return e;
+      if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
       if (p.group_tiles > 0) {  // one summary per group: out_sum is [groups][out_stride]
         const dim3 ggrid((p.B + kWaves - 1) / kWaves, p.n_tiles / p.group_tiles);
         hipLaunchKernelGGL(reduce_tiles_kernel<EPI_GROUP>, ggrid, dim3(kThreads), 0, stream, p.B, p.n_tiles,
@@ -996,7 +1000,10 @@ hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi
                            p.ws_val, p.ws_idx, p.ws_m, p.ws_s, nullptr, p.out_sum, p.n_tiles, (int64_t)0);
       }
       return hipGetLastError();
-    case EPI_STORE: return launch_stream_epi<EPI_STORE>(p, cfg, stream);
+    case EPI_STORE:
+      e = launch_stream_epi<EPI_STORE>(p, cfg, stream);
+      if (e != hipSuccess) return e;
+      return ev_after ? hipEventRecord(ev_after, stream) : hipSuccess;
     default: return hipErrorInvalidValue;
   }
 }

@@ -35,8 +35,8 @@ namespace fsk {
 // ---------------------------------------------------------------------------
 // Cross-tile reduction: a second, small launch on the same stream (the kernel
 // boundary publishes the workspace), one wave per batch row over its n_tiles
-// entries.  [FlashSampling, arXiv 2603.15854, section 3: the stage-2 reduction
-// over tiles]
+// entries.  [FlashSampling, arXiv 2603.15854, abstract: a small reduction over
+// the per-tile maximizers finishes the sample]
 // ---------------------------------------------------------------------------
 // With several groups per launch (gridDim.y groups of tpg tiles each), group
 // g reduces tiles [g * tpg, (g + 1) * tpg) into out_sum[g * out_stride + b].

@@ -63,6 +63,44 @@ def check_tiles(gmax, garg, omax, oarg, p_rows, bounds, label=""):
     return float(err.max()) if err.size else 0.0
 
 
+def kth_score(s_all, k):
+    """k-th largest finite score of a row (-inf if fewer than k are finite)."""
+    fin = np.sort(s_all[np.isfinite(s_all)].astype(np.float64))[::-1]
+    return float(fin[k - 1]) if fin.size >= k else -np.inf
+
+
+def check_ids_topk(gpu_ids, ora_ids, L_rows, rows, T, seed, step0, top_k, mask=None, label=""):
+    """check_ids for top-k sampling, with the top-k boundary reading of the near-tie rule.
+
+    gpu_ids, ora_ids: [S, R]; L_rows[r] are the oracle's logits of global row rows[r].  A
+    mismatch is accepted if it is a near tie of the final argmax among the oracle's kept ids,
+    or if the kept sets may differ at the k-th boundary: the GPU's id or the oracle's has a
+    score within 1e-3 (1 + |s_k|) of the k-th largest score s_k.  The GPU's id must always be
+    an allowed id whose score reaches s_k up to that tolerance.  Returns the mismatch count.
+    """
+    gpu_ids = np.asarray(gpu_ids)
+    ora_ids = np.asarray(ora_ids)
+    assert gpu_ids.shape == ora_ids.shape
+    mism = np.argwhere(gpu_ids != ora_ids)
+    for s, r in mism:
+        io, ig = int(ora_ids[s, r]), int(gpu_ids[s, r])
+        mrow = None if mask is None else mask[rows[r]]
+        s_all = oracle.scores_row(L_rows[r], T, mask_row=mrow).astype(np.float64)
+        assert io >= 0, f"{label}: oracle has no allowed id at step {s} row {r} but GPU chose {ig}"
+        assert 0 <= ig < s_all.shape[0] and np.isfinite(s_all[ig]), f"{label}: GPU id {ig} not allowed"
+        sk = kth_score(s_all, top_k)
+        tol_k = NEAR_TIE_REL * (1 + abs(sk)) if np.isfinite(sk) else 0.0
+        assert s_all[ig] >= sk - tol_k, f"{label}: GPU id {ig} (s={s_all[ig]}) below the k-th score {sk}"
+        p = oracle.perturbed_row(L_rows[r], T, seed, step0 + int(s), int(rows[r]), mask_row=mrow, top_k=top_k)
+        final_tie = np.isfinite(p[ig]) and float(p[io]) - float(p[ig]) < NEAR_TIE_REL * (1 + abs(float(p[io])))
+        boundary = abs(s_all[ig] - sk) < tol_k or abs(s_all[io] - sk) < tol_k
+        assert final_tie or boundary, \
+            f"{label}: step {s} row {r}: GPU {ig} vs oracle {io} (s {s_all[ig]} / {s_all[io]}, s_k {sk})"
+    frac = 1.0 - len(mism) / gpu_ids.size
+    assert frac >= ID_MATCH_MIN, f"{label}: only {frac:.5f} of rows identical"
+    return len(mism)
+
+
 def oracle_p_fn(L_rows, rows, T, seed, step0, mask=None, top_k=0):
     """p_row(s, r) for check_ids: oracle perturbed scores of L_rows[r] (global row rows[r]) at step0 + s."""
     def p_row(s, r):

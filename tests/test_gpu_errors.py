@@ -154,3 +154,47 @@ def test_context_still_samples_after_errors(env):
     rows = np.arange(4)
     want, _ = oracle.sample_rows_steps(L, rows, 1.0, 1, 2, 1)
     check_ids(got[None, :], want, oracle_p_fn(L, rows, 1.0, 1, 2), "after errors")
+
+
+def test_binding_rejects_bad_buffers_before_any_launch(env):
+    # the Python binding checks every output, workspace and mask tensor's dtype,
+    # device, layout and size, and raises before the library is called
+    import torch
+
+    fs, ctx = env
+    H, W, out = _bufs(V=1000)
+    n, _ = fs.fs_fmms_tiling(ctx, 4, 256, 1000)
+    bad_calls = {
+        "out int64": lambda: fs.fs_fmms_sample(ctx, H, W, 1.0, 0, 0, out=torch.zeros(4, dtype=torch.int64,
+                                                                                     device="cuda")),
+        "out too short": lambda: fs.fs_fmms_sample(ctx, H, W, 1.0, 0, 0, out=out[:3]),
+        "out on the host": lambda: fs.fs_fmms_sample(ctx, H, W, 1.0, 0, 0, out=torch.zeros(4, dtype=torch.int32)),
+        "out strided": lambda: fs.fs_fmms_sample(ctx, H, W, 1.0, 0, 0,
+                                                 out=torch.zeros(8, dtype=torch.int32, device="cuda")[::2]),
+        "tile_max too small": lambda: fs.fs_fmms_sample(
+            ctx, H, W, 1.0, 0, 0, out=out, tile_max=torch.zeros((4, n - 1), device="cuda"),
+            tile_arg=torch.zeros((4, n), dtype=torch.int32, device="cuda")),
+        "tile_arg float": lambda: fs.fs_fmms_sample(
+            ctx, H, W, 1.0, 0, 0, out=out, tile_max=torch.zeros((4, n), device="cuda"),
+            tile_arg=torch.zeros((4, n), device="cuda")),
+        "mask rows < B": lambda: fs.fs_fmms_sample(ctx, H, W, 1.0, 0, 0, out=out,
+                                                   mask=torch.full((3, 32), -1, dtype=torch.int32, device="cuda")),
+        "mask words < ceil(V/32)": lambda: fs.fs_fmms_sample(
+            ctx, H, W, 1.0, 0, 0, out=out, mask=torch.full((4, 31), -1, dtype=torch.int32, device="cuda")),
+        "logits_ws rows < B": lambda: fs.fs_unfused_sample(ctx, H, W, 1.0, 0, 0, out=out,
+                                                            logits_ws=torch.zeros((3, 1000), device="cuda")),
+        "logits_ws cols < V": lambda: fs.fs_softmax_sample(ctx, H, W, 1.0, 0, 0, out=out,
+                                                           logits_ws=torch.zeros((4, 996), device="cuda")),
+        "group out too short": lambda: fs.fs_group_summary(ctx, H, W[:512], 0, 1.0, 0, 0,
+                                                           out=torch.zeros((3, 3), dtype=torch.int32, device="cuda")),
+        "combine out too short": lambda: fs.fs_group_combine(
+            ctx, torch.zeros((2, 4, 3), dtype=torch.int32, device="cuda"), 0, 0, out=out[:2]),
+        "multi out too short": lambda: fs.fs_fmms_sample_multi(
+            ctx, H, W, 1.0, 0, 0, 2, out=torch.zeros(7, dtype=torch.int32, device="cuda")),
+    }
+    for label, call in bad_calls.items():
+        say(f"binding check: {label}")
+        with pytest.raises((TypeError, ValueError)):
+            call()
+    torch.cuda.synchronize()
+    assert torch.all(out == -7).item(), "a rejected call wrote its output"

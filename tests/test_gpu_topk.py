@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import check_ids, dev_bf16, dev_words, oracle_p_fn, say
+from gpu_helpers import check_ids, check_ids_topk, dev_bf16, dev_words, oracle_p_fn, say
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,31 @@ def test_topk_parity(fs, ctx, B, d, V, T, k, path):
     H = synth.normal_bf16(B, d, seed=21)
     W = synth.normal_bf16(V, d, seed=22, std=0.05)
     _check(fs, ctx, H, W, T, 3, 20, k, path=path, label=f"topk k={k}")
+
+
+@pytest.mark.parametrize("B,d,V,T,k", [
+    (4, 256, 4096, 1.0, 50),
+    (8, 520, 3000, 0.7, 5),
+    (20, 1024, 5000, 0.8, 64),
+    (33, 2048, 20011, 0.9, 50),
+    (70, 264, 333, 1.0, 17),
+])
+def test_topk_end_to_end_vs_oracle_logits(fs, ctx, B, d, V, T, k):
+    # end to end: the oracle computes its own logits from the same bf16 operands;
+    # the kept sets may differ only at the k-th boundary, the draws only at near ties
+    say(f"top-k end to end B={B} d={d} V={V} T={T} k={k}")
+    H = synth.normal_bf16(B, d, seed=41)
+    W = synth.normal_bf16(V, d, seed=42, std=0.05)
+    L = oracle.logits(H, W)
+    allowed = np.random.default_rng(43).random((B, V)) >= 0.25
+    mask = synth.pack_mask(allowed)
+    rows = np.arange(B)
+    for mnp in (None, mask):
+        md = None if mnp is None else dev_words(mnp)
+        gpu = _sample(fs, ctx, dev_bf16(H), dev_bf16(W), T, 11, range(15), k, md)
+        ora, _ = oracle.sample_rows_steps(L, rows, T, 11, 0, 15, mask=mnp, top_k=k)
+        n = check_ids_topk(gpu, ora, L, rows, T, 11, 0, k, mask=mnp, label=f"top-k e2e k={k}")
+        say(f"  mask={mnp is not None}: {n} near-tie mismatches over {gpu.size} draws")
 
 
 def test_topk_one_is_argmax(fs, ctx):
