@@ -201,6 +201,27 @@ int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh
 int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int n_groups, int B, uint64_t seed,
                      uint64_t step, int mode, int32_t* out_idx);
 
+/* Allocation-free variant of fs_fmms_sample, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It needs no context and calls no allocating routine:
+ * the per-tile winners go to a static device array of this library (512 KiB
+ * on each GPU it runs on, held until the process ends), whose device address
+ * is looked up once per GPU (by fs_create on its device, else by this call's
+ * first use on the current device).  The caller passes inputs and outputs as
+ * for fs_fmms_sample, on the current HIP device:
+ *   H [B, d], W [V, d] bf16 (row strides ldh, ldw), temperature, seed, step,
+ *   mask (NULL or [B, ldm] words), out_idx [B] int32 device.
+ * Same result as fs_fmms_sample with top_k = 0, no tile maxima and
+ * FS_PATH_AUTO (same kernels and tiling).
+ * Limits: 1 <= B <= 256 (FS_ERR_CAPACITY above), V < 2^31, and the other
+ * requirements of fs_fmms_sample.  No top-k, tile maxima or several samples.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (two streams, two threads)
+ * race and must be serialized by the caller. */
+int fs_fmms_sample_noalloc(void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw, int B,
+                           int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                           const uint32_t* mask, int64_t ldm, int32_t* out_idx);
+
 /* Timing hook for measurement.  The next streaming call made on this context
  * records `before` on its stream right before its streaming (LM-head) kernel
  * and `after` right after it, ahead of the small tile reduction that

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     fs_destroy,
     fs_fmms_sample,
     fs_fmms_sample_multi,
+    fs_fmms_sample_noalloc,
     fs_fmms_tiling,
     fs_group_combine,
     fs_group_summaries,

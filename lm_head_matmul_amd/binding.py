@@ -49,6 +49,7 @@ SIGNATURES = {
     "fs_group_summaries": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _I, _F, _U64, _U64, _P, _I64, _P,
                                 _I]),
     "fs_group_combine": (_I, [_P, _P, _P, _I, _I, _U64, _U64, _I, _P]),
+    "fs_fmms_sample_noalloc": (_I, [_P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _P]),
     "fs_profile_next_launch": (_I, [_P, _P, _P]),
     "fs_debug_philox": (_I, [_P, _P, _U64, _U64, _I, _I64, _I64, _P, _P]),
     "fs_debug_gumbel_bits": (_I, [_P, _P, _U64, _I64, _P]),
@@ -200,6 +201,24 @@ def fs_fmms_sample_multi(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature
     mptr, ldm = _mask_args(mask, B, V)
     _check(_lib.fs_fmms_sample_multi(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                      float(temperature), seed, step, mptr, ldm, num_samples, out.data_ptr(), path))
+    return out
+
+
+def fs_fmms_sample_noalloc(H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+                           mask: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """fs_fmms_sample without a context (no top-k, tile maxima or path choice), on H's device."""
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=H.device)
+    _device_buffer(out, torch.int32, B, "out")
+    mptr, ldm = _mask_args(mask, B, V)
+    with torch.cuda.device(H.device):
+        _check(_lib.fs_fmms_sample_noalloc(_stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
+                                           float(temperature), seed, step, mptr, ldm, out.data_ptr()))
     return out
 
 

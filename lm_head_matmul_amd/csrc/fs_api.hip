@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/flashsampling.h"
 #include "fs_kernels.h"
@@ -266,6 +267,51 @@ int launch_topk(const fs_ctx* ctx, const float* logits, int64_t ldl, int rows, i
   return FS_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free sampling (fs_fmms_sample_noalloc).  Its per-tile winners --
+// the only device memory the plain sampler needs beyond the caller's inputs
+// and outputs -- live in one file-scope device array instead of a context's
+// workspace: [kNoAllocMaxB][kNoAllocMaxTiles] fp32 values, then as many int32
+// ids.  Each GPU holds its own copy of the array until the process ends.  In
+// host code `scratch` only names the symbol; its device address on each GPU
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr int kNoAllocMaxB = 256;
+constexpr int kNoAllocMaxTiles = 256;
+constexpr size_t kNoAllocScratchBytes = (size_t)kNoAllocMaxB * kNoAllocMaxTiles * 8;  // 512 KiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+struct NoAllocDevice {
+  unsigned char* ptr;  // device address of this GPU's copy of `scratch` (null: not set up yet)
+  int n_cu;
+};
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+
+// Looks up (once per device) the address of the device's `scratch`; `dev` must be current.
+int noalloc_setup(int dev, NoAllocDevice& out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(FS_ERR_UNSUPPORTED, "device %d: the allocation-free path supports devices 0..%d", dev,
+                kNoAllocMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoAllocDevice& d = g_noalloc[dev];
+  if (d.ptr == nullptr) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(FS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    int n_cu = 0;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    d.n_cu = n_cu;
+    d.ptr = (unsigned char*)ptr;
+  }
+  out = d;
+  return FS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,6 +342,14 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     return hip_fail(e, "hipDeviceGetAttribute");
   }
   c->max_tiles = c->n_cu;
+  {  // the allocation-free entry point's scratch address on this device, looked up at set-up
+    NoAllocDevice nd;
+    const int rc = noalloc_setup(device, nd);
+    if (rc != FS_OK) {
+      delete c;
+      return rc;
+    }
+  }
   const size_t n = (size_t)max_B * (size_t)c->max_tiles;
   const size_t bytes = 4 * n * sizeof(float) + 256;
   e = hipMalloc(&c->base, bytes);
@@ -631,6 +685,35 @@ int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int
                                            mode, out_idx, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return FS_OK;
+}
+
+int fs_fmms_sample_noalloc(void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw, int B,
+                           int d, int64_t V, float temperature, uint64_t seed, uint64_t step, const uint32_t* mask,
+                           int64_t ldm, int32_t* out_idx) {
+  if (B < 1 || B > kNoAllocMaxB)
+    return fail(B < 1 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY,
+                "B=%d outside [1, %d]: the allocation-free path's static scratch holds %d rows of tile winners",
+                B, kNoAllocMaxB, kNoAllocMaxB);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  NoAllocDevice nd;
+  const int rc = noalloc_setup(dev, nd);
+  if (rc != FS_OK) return rc;
+  // a context on the stack over the static scratch: the same checks, kernels and
+  // tiling as fs_fmms_sample, which never allocates once given a workspace
+  fs_ctx c;
+  std::memset(&c, 0, sizeof c);
+  c.device = dev;
+  c.max_B = kNoAllocMaxB;
+  c.max_V = INT32_MAX;
+  c.max_top_k = 0;
+  c.n_cu = nd.n_cu;
+  c.max_tiles = nd.n_cu < kNoAllocMaxTiles ? nd.n_cu : kNoAllocMaxTiles;
+  c.ws_val = (float*)nd.ptr;
+  c.ws_idx = (int32_t*)(nd.ptr + (size_t)kNoAllocMaxB * kNoAllocMaxTiles * sizeof(float));
+  return fs_fmms_sample(&c, stream, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm, 0, out_idx, nullptr,
+                        nullptr, FS_PATH_AUTO);
 }
 
 int fs_profile_next_launch(fs_ctx* ctx, void* before, void* after) {
