@@ -40,17 +40,17 @@ def lib():
             "fso_gumbel_scan": (None, [u64, u64, P, P]),
             "fso_logits": (None, [P, i64, P, i64, i32, i32, i64, P]),
             "fso_logits_fp32acc": (None, [P, i64, P, i64, i32, i32, i64, P]),
-            "fso_scores_row": (None, [P, i64, f32, P, i32, P]),
-            "fso_perturbed_row": (None, [P, i64, f32, u64, u64, i32, P, i32, P]),
+            "fso_scores_row": (None, [P, i64, f32, P, i32, f32, P]),
+            "fso_perturbed_row": (None, [P, i64, f32, u64, u64, i32, P, i32, f32, P]),
             "fso_argmax": (i64, [P, i64]),
-            "fso_sample_from_logits": (None, [P, i32, i64, f32, u64, u64, P, i64, i32, P, P]),
-            "fso_sample_steps": (None, [P, i32, i64, f32, u64, u64, i64, P, i64, i32, P]),
-            "fso_sample_rows_steps": (None, [P, P, i32, i64, f32, u64, u64, i64, P, i64, i32, P, P]),
+            "fso_sample_from_logits": (None, [P, i32, i64, f32, u64, u64, P, i64, i32, f32, P, P]),
+            "fso_sample_steps": (None, [P, i32, i64, f32, u64, u64, i64, P, i64, i32, f32, P]),
+            "fso_sample_rows_steps": (None, [P, P, i32, i64, f32, u64, u64, i64, P, i64, i32, f32, P, P]),
             "fso_tile_maxima": (None, [P, i32, i64, f32, u64, u64, P, i64, P, i32, P, P]),
             "fso_group_summary": (None, [P, i32, i64, i64, i64, f32, u64, u64, P, i64, P, P, P]),
             "fso_group_combine": (None, [P, P, P, i32, i32, u64, u64, i32, P]),
             "fso_grouped_sample_steps": (None, [P, i32, i64, f32, u64, u64, i64, P, i64, P, i32, i32, P]),
-            "fso_fmms_sample": (None, [P, i64, P, i64, i32, i32, i64, f32, u64, u64, P, i64, i32, P]),
+            "fso_fmms_sample": (None, [P, i64, P, i64, i32, i32, i64, f32, u64, u64, P, i64, i32, f32, P]),
             "fso_num_threads": (i32, []),
             "fso_uniform_bits": (u32, [u64, u64, u32]),
             "fso_uniform64": (ctypes.c_double, [u32]),
@@ -146,19 +146,19 @@ def _mask_args(mask, B):
     return m, m.shape[1]
 
 
-def scores_row(logit_row, T, mask_row=None, top_k=0):
+def scores_row(logit_row, T, mask_row=None, top_k=0, top_p=1.0):
     x = _c(logit_row, np.float32)
     m = None if mask_row is None else _c(mask_row, np.uint32)
     out = np.empty_like(x)
-    lib().fso_scores_row(_ptr(x), x.shape[0], T, _ptr(m), top_k, _ptr(out))
+    lib().fso_scores_row(_ptr(x), x.shape[0], T, _ptr(m), top_k, top_p, _ptr(out))
     return out
 
 
-def perturbed_row(logit_row, T, seed, step, row, mask_row=None, top_k=0):
+def perturbed_row(logit_row, T, seed, step, row, mask_row=None, top_k=0, top_p=1.0):
     x = _c(logit_row, np.float32)
     m = None if mask_row is None else _c(mask_row, np.uint32)
     out = np.empty_like(x)
-    lib().fso_perturbed_row(_ptr(x), x.shape[0], T, seed, step, row, _ptr(m), top_k, _ptr(out))
+    lib().fso_perturbed_row(_ptr(x), x.shape[0], T, seed, step, row, _ptr(m), top_k, top_p, _ptr(out))
     return out
 
 
@@ -167,24 +167,24 @@ def argmax(p) -> int:
     return int(lib().fso_argmax(_ptr(p), p.shape[0]))
 
 
-def sample_from_logits(L, T, seed, step, mask=None, top_k=0, want_p=False):
+def sample_from_logits(L, T, seed, step, mask=None, top_k=0, want_p=False, top_p=1.0):
     """One step: returns out_idx [B] (int32) and, if asked, p [B, V]."""
     L = _c(L, np.float32)
     B, V = L.shape
     m, ldm = _mask_args(mask, B)
     out = np.empty(B, np.int32)
     p = np.empty((B, V), np.float32) if want_p else None
-    lib().fso_sample_from_logits(_ptr(L), B, V, T, seed, step, _ptr(m), ldm, top_k, _ptr(out), _ptr(p))
+    lib().fso_sample_from_logits(_ptr(L), B, V, T, seed, step, _ptr(m), ldm, top_k, top_p, _ptr(out), _ptr(p))
     return (out, p) if want_p else out
 
 
-def sample_steps(L, T, seed, step0, nsteps, mask=None, top_k=0):
+def sample_steps(L, T, seed, step0, nsteps, mask=None, top_k=0, top_p=1.0):
     """[nsteps, B] samples for steps step0 .. step0 + nsteps - 1."""
     L = _c(L, np.float32)
     B, V = L.shape
     m, ldm = _mask_args(mask, B)
     out = np.empty((nsteps, B), np.int32)
-    lib().fso_sample_steps(_ptr(L), B, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, _ptr(out))
+    lib().fso_sample_steps(_ptr(L), B, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, top_p, _ptr(out))
     return out
 
 
@@ -216,7 +216,7 @@ def cdf_sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None):
     return ids, u
 
 
-def sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None, top_k=0):
+def sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None, top_k=0, top_p=1.0):
     """Samples of global rows `rows` (logits L[i] belong to row rows[i]) for nsteps steps.
 
     Returns (ids, pmax), each [nsteps, R].  mask, if given, is the full [B, ldm] mask.
@@ -229,7 +229,8 @@ def sample_rows_steps(L, rows, T, seed, step0, nsteps, mask=None, top_k=0):
     ldm = 0 if m is None else m.shape[1]
     ids = np.empty((nsteps, R), np.int32)
     pmax = np.empty((nsteps, R), np.float32)
-    lib().fso_sample_rows_steps(_ptr(L), _ptr(rows), R, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, _ptr(ids),
+    lib().fso_sample_rows_steps(_ptr(L), _ptr(rows), R, V, T, seed, step0, nsteps, _ptr(m), ldm, top_k, top_p,
+                                _ptr(ids),
                                 _ptr(pmax))
     return ids, pmax
 
@@ -281,7 +282,7 @@ def grouped_sample_steps(L, T, seed, step0, nsteps, bounds, mode, mask=None):
     return out
 
 
-def fmms_sample(H, W, T, seed, step, mask=None, top_k=0):
+def fmms_sample(H, W, T, seed, step, mask=None, top_k=0, top_p=1.0):
     """End to end from bf16 operands: [B] sampled ids."""
     H = _c(H, np.uint16)
     W = _c(W, np.uint16)
@@ -289,5 +290,5 @@ def fmms_sample(H, W, T, seed, step, mask=None, top_k=0):
     V = W.shape[0]
     m, ldm = _mask_args(mask, B)
     out = np.empty(B, np.int32)
-    lib().fso_fmms_sample(_ptr(H), d, _ptr(W), d, B, d, V, T, seed, step, _ptr(m), ldm, top_k, _ptr(out))
+    lib().fso_fmms_sample(_ptr(H), d, _ptr(W), d, B, d, V, T, seed, step, _ptr(m), ldm, top_k, top_p, _ptr(out))
     return out

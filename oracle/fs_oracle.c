@@ -51,6 +51,15 @@
  *       range the vocabulary never reaches; k* = argmax_k (lse_k + g'_k), the
  *       sample is that group's own argmax.  Mode M: k* = argmax_k pmax_k,
  *       which reproduces the flat argmax exactly.
+ *   R10 top-p (nucleus) sampling, which two pages call compatible with the
+ *       method without giving one, follows top-k: among the kept ids, sorted by
+ *       score (descending, lower id first), the weights w = exp(s - s_max) are
+ *       summed in fp64 in that order, and an id is kept while the weight of
+ *       the ids before it is below top_p times their total (the shortest
+ *       prefix whose mass reaches top_p of the kept mass).  top_p = 1 keeps
+ *       every top-k id.  [nucleus sampling as defined by Holtzman et al., "The
+ *       Curious Case of Neural Text Degeneration", ICLR 2020; cjcn.com.cn and
+ *       news.neo-ai.one FlashSampling articles: compatible with top-p]
  *   R9  conventional comparator (not the method): one uniform per row and step
  *       from word 0 of Philox(key = seed, counter = (0x80000000, row, step)),
  *       u = (r+1)/(2^32+1); the sample is the first allowed id whose running
@@ -249,9 +258,38 @@ static int by_score_desc_id_asc(const void* pa, const void* pb) {
   return (a->id > b->id) - (a->id < b->id);
 }
 
-/* Scaled, masked, top-k-filtered scores of one row (R2, R5, R6).
+/* Top-p within the ids a row keeps (R10): s holds V scores, -inf for ids
+ * already excluded; ids past the nucleus are set to -inf. */
+static void nucleus_filter(float* s, int64_t V, float top_p) {
+  int64_t n = 0;
+  for (int64_t v = 0; v < V; ++v)
+    if (s[v] != -INFINITY && s[v] == s[v]) ++n;
+  if (n == 0) return;
+  scored_id* list = (scored_id*)malloc((size_t)n * sizeof(scored_id));
+  int64_t i = 0;
+  for (int64_t v = 0; v < V; ++v)
+    if (s[v] != -INFINITY && s[v] == s[v]) {
+      list[i].s = s[v];
+      list[i].id = v;
+      ++i;
+    }
+  qsort(list, (size_t)n, sizeof(scored_id), by_score_desc_id_asc);
+  const double m = (double)list[0].s;
+  double total = 0.0;
+  for (i = 0; i < n; ++i) total += exp((double)list[i].s - m);
+  double before = 0.0; /* weight of the ids ahead of list[i] */
+  for (i = 0; i < n; ++i) {
+    const double w = exp((double)list[i].s - m);
+    if (!(before < (double)top_p * total)) s[list[i].id] = -INFINITY;
+    before += w;
+  }
+  free(list);
+}
+
+/* Scaled, masked, top-k-filtered scores of one row (R2, R5, R6), then the
+ * nucleus of the kept ids when top_p < 1 (R10).
  * s_out has V entries; excluded ids hold -inf. */
-void fso_scores_row(const float* logit_row, int64_t V, float T, const uint32_t* mask_row, int top_k,
+void fso_scores_row(const float* logit_row, int64_t V, float T, const uint32_t* mask_row, int top_k, float top_p,
                     float* s_out) {
   for (int64_t v = 0; v < V; ++v) {
     float s = logit_row[v] / T;
@@ -276,12 +314,13 @@ void fso_scores_row(const float* logit_row, int64_t V, float T, const uint32_t* 
       free(list);
     }
   }
+  if (top_p < 1.0f) nucleus_filter(s_out, V, top_p);
 }
 
 /* Perturbed scores p = s + g of one row (R1, R4). */
 void fso_perturbed_row(const float* logit_row, int64_t V, float T, uint64_t seed, uint64_t step, int row,
-                       const uint32_t* mask_row, int top_k, float* p_out) {
-  fso_scores_row(logit_row, V, T, mask_row, top_k, p_out);
+                       const uint32_t* mask_row, int top_k, float top_p, float* p_out) {
+  fso_scores_row(logit_row, V, T, mask_row, top_k, top_p, p_out);
   for (int64_t v = 0; v < V; ++v) {
     float g = fso_gumbel32(fso_noise_bits(seed, step, (uint32_t)row, (uint32_t)v));
     p_out[v] = p_out[v] + g; /* -inf stays -inf */
@@ -303,12 +342,13 @@ int64_t fso_argmax(const float* p, int64_t n) {
 /* One sampling step for B rows from logits [B, V] (row stride V).
  * mask: NULL or [B, ldm] words.  p_out: NULL or [B, V] perturbed scores. */
 void fso_sample_from_logits(const float* logits, int B, int64_t V, float T, uint64_t seed, uint64_t step,
-                            const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* p_out) {
+                            const uint32_t* mask, int64_t ldm, int top_k, float top_p, int32_t* out_idx,
+                            float* p_out) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int b = 0; b < B; ++b) {
     float* p = p_out ? p_out + (int64_t)b * V : (float*)malloc((size_t)V * sizeof(float));
     fso_perturbed_row(logits + (int64_t)b * V, V, T, seed, step, b, mask ? mask + (int64_t)b * ldm : NULL,
-                      top_k, p);
+                      top_k, top_p, p);
     out_idx[b] = (int32_t)fso_argmax(p, V);
     if (!p_out) free(p);
   }
@@ -324,7 +364,7 @@ void fso_sample_from_logits(const float* logits, int B, int64_t V, float T, uint
  * exponentiates, normalizes and scans a cumulative array to pick a token] */
 int64_t fso_cdf_sample_row(const float* logit_row, int64_t V, float T, const uint32_t* mask_row, double u) {
   float* s = (float*)malloc((size_t)V * sizeof(float));
-  fso_scores_row(logit_row, V, T, mask_row, 0, s);
+  fso_scores_row(logit_row, V, T, mask_row, 0, 1.0f, s);
   double m = -INFINITY;
   int64_t last = -1;
   for (int64_t v = 0; v < V; ++v)
@@ -371,13 +411,13 @@ void fso_cdf_sample_rows_steps(const float* logits, const int32_t* rows, int R, 
 /* Many consecutive steps step0 .. step0+nsteps-1 for fixed logits; out is
  * [nsteps, B].  Used by the distributional tests. */
 void fso_sample_steps(const float* logits, int B, int64_t V, float T, uint64_t seed, uint64_t step0,
-                      int64_t nsteps, const uint32_t* mask, int64_t ldm, int top_k, int32_t* out) {
+                      int64_t nsteps, const uint32_t* mask, int64_t ldm, int top_k, float top_p, int32_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < nsteps; ++t) {
     float* p = (float*)malloc((size_t)V * sizeof(float));
     for (int b = 0; b < B; ++b) {
       fso_perturbed_row(logits + (int64_t)b * V, V, T, seed, step0 + (uint64_t)t, b,
-                        mask ? mask + (int64_t)b * ldm : NULL, top_k, p);
+                        mask ? mask + (int64_t)b * ldm : NULL, top_k, top_p, p);
       out[t * B + b] = (int32_t)fso_argmax(p, V);
     }
     free(p);
@@ -390,13 +430,13 @@ void fso_sample_steps(const float* logits, int B, int64_t V, float T, uint64_t s
  * the sampled id and its perturbed score. */
 void fso_sample_rows_steps(const float* logits, const int32_t* rows, int R, int64_t V, float T, uint64_t seed,
                            uint64_t step0, int64_t nsteps, const uint32_t* mask, int64_t ldm, int top_k,
-                           int32_t* out_idx, float* out_pmax) {
+                           float top_p, int32_t* out_idx, float* out_pmax) {
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int64_t t = 0; t < nsteps; ++t) {
     for (int i = 0; i < R; ++i) {
       float* p = (float*)malloc((size_t)V * sizeof(float));
       fso_perturbed_row(logits + (int64_t)i * V, V, T, seed, step0 + (uint64_t)t, rows[i],
-                        mask ? mask + (int64_t)rows[i] * ldm : NULL, top_k, p);
+                        mask ? mask + (int64_t)rows[i] * ldm : NULL, top_k, top_p, p);
       int64_t a = fso_argmax(p, V);
       out_idx[t * R + i] = (int32_t)a;
       out_pmax[t * R + i] = a < 0 ? -INFINITY : p[a];
@@ -414,7 +454,7 @@ void fso_tile_maxima(const float* logits, int B, int64_t V, float T, uint64_t se
   for (int b = 0; b < B; ++b) {
     float* p = (float*)malloc((size_t)V * sizeof(float));
     fso_perturbed_row(logits + (int64_t)b * V, V, T, seed, step, b, mask ? mask + (int64_t)b * ldm : NULL, 0,
-                      p);
+                      1.0f, p);
     for (int i = 0; i < n_tiles; ++i) {
       int64_t lo = bounds[i], hi = bounds[i + 1];
       int64_t a = fso_argmax(p + lo, hi - lo);
@@ -514,7 +554,7 @@ void fso_grouped_sample_steps(const float* logits, int B, int64_t V, float T, ui
     int32_t* arg = (int32_t*)malloc((size_t)n_groups * (size_t)B * sizeof(int32_t));
     for (int b = 0; b < B; ++b) {
       const uint32_t* mrow = mask ? mask + (int64_t)b * ldm : NULL;
-      fso_scores_row(logits + (int64_t)b * V, V, T, mrow, 0, s);
+      fso_scores_row(logits + (int64_t)b * V, V, T, mrow, 0, 1.0f, s);
       for (int64_t v = 0; v < V; ++v) p[v] = s[v] + fso_gumbel32(fso_noise_bits(seed, step, (uint32_t)b, (uint32_t)v));
       for (int k = 0; k < n_groups; ++k)
         group_summary_row(s, p, bounds[k], bounds[k + 1], &lse[(int64_t)k * B + b], &pmax[(int64_t)k * B + b],
@@ -534,10 +574,10 @@ void fso_grouped_sample_steps(const float* logits, int B, int64_t V, float T, ui
 /* ------------------------------------------------------------------------ */
 void fso_fmms_sample(const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw, int B, int d, int64_t V,
                      float T, uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm, int top_k,
-                     int32_t* out_idx) {
+                     float top_p, int32_t* out_idx) {
   float* logits = (float*)malloc((size_t)B * (size_t)V * sizeof(float));
   fso_logits(H, ldh, W, ldw, B, d, V, logits);
-  fso_sample_from_logits(logits, B, V, T, seed, step, mask, ldm, top_k, out_idx, NULL);
+  fso_sample_from_logits(logits, B, V, T, seed, step, mask, ldm, top_k, top_p, out_idx, NULL);
   free(logits);
 }
 
