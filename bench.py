@@ -30,7 +30,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/step and achieved HBM GB/s (% of peak) for FMMS at V=151936, B=1–64"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fmms_mid_decode_B64_hbm_traffic.md")
+# the calls a --profile run can time: fs_fmms_sample (top_k) or the unfused comparator
+PROFILE_OPS = {"fused": dict(top_k=0, unfused=False), "unfused": dict(top_k=0, unfused=True),
+               "topk": dict(top_k=50, unfused=False)}
+
+
+def traffic_summary_path(op, workload="mid_decode", B=64):
+    return os.path.join(ROOT, "profiles", f"{op}_{workload}_B{B}_hbm_traffic.md")
+
+
 CSRC = os.path.join(ROOT, "lm_head_matmul_amd", "csrc")
 KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
 CALIB_BYTES = 1 << 30  # the --profile run's plain device fill + copy
@@ -49,9 +57,12 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: one 1 GiB device copy (counter calibration), then the "
-                         "headline steps only")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
-                    help="write the profiles/ summaries from a --profile run's rocprofv3 csv output and exit")
+                         "headline steps only, of the call --profile-op names")
+    ap.add_argument("--profile-op", default="fused", choices=sorted(PROFILE_OPS),
+                    help="the call a --profile run times: the fused sampler, the unfused comparator, or top-k")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the profiles/ summaries of a --profile run's rocprofv3 csv output (for the "
+                         "--profile-op, --workload and --batch given) and exit")
     return ap.parse_args()
 
 
@@ -77,12 +88,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it matches these kernels."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def measured_traffic(op="fused", workload="mid_decode", B=64):
+    """HBM bytes per step of a call from its committed counter summary, if it matches these kernels."""
+    path = traffic_summary_path(op, workload, B)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_SUMMARY) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and line.strip().startswith("- "):
                 k, v = line.strip()[2:].split(":", 1)
@@ -90,56 +102,61 @@ def measured_traffic():
     if vals.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return int(float(vals["hbm_bytes_per_launch"]))
+        return int(float(vals["hbm_bytes_per_step"]))
     except (KeyError, ValueError):
         return None
 
 
-PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace "
-             "-- python3 bench.py --profile --steps 1000 --warmup 50",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch "
-             "-- python3 bench.py --profile --steps 5 --warmup 2",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write "
-             "-- python3 bench.py --profile --steps 5 --warmup 2",
-}
-
-def headline_kernel_name(names):
-    """The streaming kernel of the step: the library's kernel with the largest total time."""
-    ours = [n for n in names if "fsk::" in n and "reduce_tiles" not in n]
-    return ours[0] if ours else None
+def profile_cmds(op, workload, B):
+    a = f"--profile --profile-op {op} --workload {workload} --batch {B}"
+    return {
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{op}_trace -o trace "
+                 f"-- python3 bench.py {a} --steps 1000 --warmup 50",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_{op}_fetch -o fetch "
+                 f"-- python3 bench.py {a} --steps 5 --warmup 2",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_{op}_write -o write "
+                 f"-- python3 bench.py {a} --steps 5 --warmup 2",
+    }
 
 
-def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B=64):
-    """Turn a --profile run's rocprofv3 csv files into the two committed text summaries."""
+def summarize_profiles(trace_csv, fetch_csv, write_csv, op="fused", workload="mid_decode", B=64):
+    """Turn a --profile run's rocprofv3 csv files into the committed text summaries of that call:
+    the kernel trace (per-kernel durations) and the HBM traffic per step (FETCH_SIZE + WRITE_SIZE
+    of every library kernel of a step, calibrated against a plain fill and copy)."""
     import csv
     import synth
 
     w = synth.WORKLOADS[workload]
     algo = algorithmic_bytes(B, w["d"], w["V"])
-    tag = f"{workload}_B{B}"
+    tag = f"{op}_{workload}_B{B}"
     pre = "cd /tmp && export TMPDIR=/tmp && cd <repo root> && "
+    cmds = profile_cmds(op, workload, B)
 
-    stats = sorted(csv.DictReader(open(trace_csv)), key=lambda r: -float(r["TotalDurationNs"]))
-    kname = headline_kernel_name([r["Name"] for r in stats])
-    assert kname is not None, "no library kernel in the trace"
-    head = [r for r in stats if r["Name"] == kname]
-    avg_us = float(head[0]["AverageNs"]) / 1e3
-    short = kname.split("(")[0].split("::")[-1].split("<")[0]
-    lines = [f"# {short}: {workload} head (B={B}, d={w['d']}, V={w['V']}), kernel trace", "",
-             f"headline kernel: `{kname}`", "",
-             f"command: `{pre}{PROFILE_CMDS['trace']}`", "",
-             "The run: one 1 GiB device fill and copy (counter calibration), 50 warmup and 1000 timed steps.", "",
-             "| kernel | calls | average us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|"]
-    for r in stats:
-        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    lines += ["", f"- headline_kernel_average_us: {avg_us:.2f}",
-              f"- algorithmic_bytes_per_launch: {algo}",
-              f"- achieved_GB_per_s_at_trace_average: {algo / (avg_us * 1e-6) / 1e9:.1f}",
+    per = {}  # the library's kernels: durations of every call
+    for r in csv.DictReader(open(trace_csv)):
+        if "fsk::" in r["Kernel_Name"]:
+            per.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    ours = sorted(per, key=lambda n: -sum(per[n]))
+    assert ours, "no library kernel in the trace"
+    stream = ours[0]  # the streaming kernel: the step's longest
+    steps = len(per[stream])
+    lines = [f"# {op}: {workload} head (B={B}, d={w['d']}, V={w['V']}), kernel trace", "",
+             f"command: `{pre}{cmds['trace']}`", "",
+             "The run: one 1 GiB device fill and copy (counter calibration), then the call's warmup, a pre-run of "
+             "at least 0.5 s, 1000 timed steps and 1000 steps with the timing events.", "",
+             "| kernel | calls | average us | median us | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
+    for n in ours:
+        d = sorted(per[n])
+        lines.append(f"| `{n.split('(')[0][:110]}` | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
+                     f"{d[len(d) // 2] / 1e3:.1f} | {d[0] / 1e3:.1f} | {d[-1] / 1e3:.1f} |")
+    avg_us = sum(per[stream]) / steps / 1e3
+    lines += ["", f"- streaming_kernel: `{stream.split('(')[0]}`",
+              f"- streaming_kernel_average_us: {avg_us:.2f}",
+              f"- library_kernels_us_per_step: {sum(sum(v) for v in per.values()) / steps / 1e3:.2f}",
+              f"- algorithmic_bytes_per_step: {algo}",
+              f"- achieved_GB_per_s_at_streaming_kernel_average: {algo / (avg_us * 1e-6) / 1e9:.1f}",
               f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
-    path = os.path.join(ROOT, "profiles", f"{short}_{tag}_kernel_trace.md")
-    open(path, "w").write("\n".join(lines))
+    open(os.path.join(ROOT, "profiles", f"{tag}_kernel_trace.md"), "w").write("\n".join(lines))
 
     def rows(fn):
         return list(csv.DictReader(open(fn)))
@@ -151,32 +168,41 @@ def summarize_profiles(trace_csv, fetch_csv, write_csv, workload="mid_decode", B
         kib = float((rs[fill] if counter == "WRITE_SIZE" else copy)["Counter_Value"])
         return (CALIB_BYTES / 1024) / kib, kib
 
+    def per_kernel(rs):
+        d = {}
+        for r in rs:
+            if "fsk::" in r["Kernel_Name"]:
+                d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return d
+
     fr, wr = rows(fetch_csv), rows(write_csv)
     f_fac, f_cal = calib(fr, "FETCH_SIZE")
     w_fac, w_cal = calib(wr, "WRITE_SIZE")
-    f_k = [float(r["Counter_Value"]) for r in fr if r["Kernel_Name"] == kname]
-    w_k = [float(r["Counter_Value"]) for r in wr if r["Kernel_Name"] == kname]
-    assert f_k and w_k, "the headline kernel is missing from a counter pass"
-    f_kib, w_kib = sum(f_k) / len(f_k), sum(w_k) / len(w_k)
-    hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
-    lines = [f"# {short}: {workload} head (B={B}, d={w['d']}, V={w['V']}), HBM traffic per launch", "",
-             f"kernel: `{kname}`", "",
-             f"fetch pass: `{pre}{PROFILE_CMDS['fetch']}`", "",
-             f"write pass: `{pre}{PROFILE_CMDS['write']}`", "",
+    fk, wk = per_kernel(fr), per_kernel(wr)
+    n_f, n_w = len(fk.get(stream, [])), len(wk.get(stream, []))
+    assert n_f and n_w, "the streaming kernel is missing from a counter pass"
+    f_step = sum(sum(v) for v in fk.values()) / n_f * 1024 * f_fac
+    w_step = sum(sum(v) for v in wk.values()) / n_w * 1024 * w_fac
+    hbm = f_step + w_step
+    lines = [f"# {op}: {workload} head (B={B}, d={w['d']}, V={w['V']}), HBM traffic per step", "",
+             f"fetch pass: `{pre}{cmds['fetch']}`", "",
+             f"write pass: `{pre}{cmds['write']}`", "",
              "Calibration: the same runs first fill 1 GiB (a pure write) and copy it (a 1 GiB read + write).",
              f"FETCH_SIZE reads {f_cal:.1f} KiB for the copy's 1048576 KiB read (factor {f_fac:.5f});",
              f"WRITE_SIZE reads {w_cal:.1f} KiB for the fill's 1048576 KiB write (factor {w_fac:.5f}).",
-             f"Kernel dispatches seen: {len(f_k)} (fetch pass), {len(w_k)} (write pass).", "",
-             f"- fetch_kib_per_launch_raw: {f_kib:.1f}",
-             f"- write_kib_per_launch_raw: {w_kib:.1f}",
-             f"- fetch_scale: {f_fac:.5f}",
-             f"- write_scale: {w_fac:.5f}",
-             f"- hbm_bytes_per_launch: {hbm:.0f}",
-             f"- algorithmic_bytes_per_launch: {algo}",
-             f"- traffic_over_algorithmic: {hbm / algo:.4f}",
-             f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
-    open(TRAFFIC_SUMMARY, "w").write("\n".join(lines))
-    print(f"wrote {path} and {TRAFFIC_SUMMARY}: avg {avg_us:.1f} us, traffic {hbm / algo:.4f} x algorithmic")
+             f"Steps seen: {n_f} (fetch pass), {n_w} (write pass); every library kernel of a step counts.", "",
+             "| kernel | FETCH_SIZE KiB per call (raw) | WRITE_SIZE KiB per call (raw) |", "|---|---:|---:|"]
+    for n in sorted(set(fk) | set(wk), key=lambda n: -sum(fk.get(n, [0.0]))):
+        fv, wv = fk.get(n, [0.0]), wk.get(n, [0.0])
+        lines.append(f"| `{n.split('(')[0][:110]}` | {sum(fv) / len(fv):.1f} | {sum(wv) / len(wv):.1f} |")
+    lines += ["", f"- fetch_bytes_per_step: {f_step:.0f}",
+              f"- write_bytes_per_step: {w_step:.0f}",
+              f"- hbm_bytes_per_step: {hbm:.0f}",
+              f"- algorithmic_bytes_per_step: {algo}",
+              f"- traffic_over_algorithmic: {hbm / algo:.4f}",
+              f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
+    open(traffic_summary_path(op, workload, B), "w").write("\n".join(lines))
+    print(f"wrote the {tag} summaries: streaming kernel {avg_us:.1f} us, traffic {hbm / algo:.4f} x algorithmic")
 
 
 class Timer:
@@ -241,7 +267,7 @@ class Timer:
 def main():
     args = parse_args()
     if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles)
+        summarize_profiles(*args.summarize_profiles, op=args.profile_op, workload=args.workload, B=args.batch)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the sampler runs on one GPU: --gpus must be 1", "n_gpus": args.gpus}),
@@ -314,8 +340,15 @@ def main():
     Hh = H_for(args.workload, B)
     outh = torch.empty(B, dtype=torch.int32, device=dev)
 
+    op = PROFILE_OPS[args.profile_op] if args.profile else PROFILE_OPS["fused"]
+    lg_h = torch.empty((B, (V + 3) // 4 * 4), dtype=torch.float32, device=dev) if op["unfused"] else None
+
     def hstep(i, base):
-        fs.fs_fmms_sample(ctx, Hh, Wsh[i % len(Wsh)], T, 0, base + i, out=outh)
+        if op["unfused"]:
+            fs.fs_unfused_sample(ctx, Hh, Wsh[i % len(Wsh)], T, 0, base + i, top_k=op["top_k"], out=outh,
+                                 logits_ws=lg_h)
+        else:
+            fs.fs_fmms_sample(ctx, Hh, Wsh[i % len(Wsh)], T, 0, base + i, top_k=op["top_k"], out=outh)
 
     log(f"headline {args.workload} B={B} d={d} V={V}: {args.warmup} warmup + {args.steps} timed steps")
     # the driver's warmup, then the same K steps timed at once: what a fresh process sees
@@ -348,6 +381,7 @@ def main():
         ms_u, _ = time_fmms(args.workload, B, min(args.steps, 200), 10, T, unfused=True)
         log(f"headline unfused: {ms_u * 1e3:.1f} us/step")
 
+    tr = {o: measured_traffic(o, args.workload, B) for o in PROFILE_OPS}
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -374,7 +408,10 @@ def main():
                    "unfused_us_per_step": None if ms_u is None else round(ms_u * 1e3, 2),
                    "fused_speedup_vs_unfused": None if ms_u is None else round(ms_u / ms, 3)},
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": tr["fused"],
+                     "traffic_unfused": tr["unfused"], "traffic_top50": tr["topk"],
+                     "hbm_bytes_saved_vs_unfused_per_step": (None if tr["fused"] is None or tr["unfused"] is None
+                                                             else tr["unfused"] - tr["fused"]),
                      "algorithmic_bytes_per_launch": algo,
                      "kernel_us": round(kern_ms * 1e3, 2),
                      "note": "achieved = algorithmic bytes of one launch / the streaming kernel's mean duration "

@@ -71,7 +71,10 @@ typedef struct {
 
 /* Create a context on `device` for calls with B <= max_B, V <= max_V and
  * top_k <= max_top_k.  Allocates the device workspace once; no later call
- * allocates device memory.  *out is set to NULL on failure. */
+ * allocates device memory.  With max_top_k > 0 the workspace holds the fused
+ * top-k's candidate lists (min(max_B, 64) rows x 256 tiles x 320 bytes);
+ * with max_top_k > 64 also min(max_B, 64) rows of max_V fp32 scores.
+ * *out is set to NULL on failure. */
 int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k);
 
 /* Release a context and its workspace (NULL is ignored).  Work that used the
@@ -110,11 +113,38 @@ int fs_fmms_tiling(fs_ctx* ctx, int B, int d, int64_t V, int path, int64_t* n_ti
  *       receiving each tile's maximum perturbed score and its id (top_k == 0
  *       only); for tests.
  * path: FS_PATH_AUTO, or force the dot-product or MFMA streaming kernel.
+ * top_k: 0 (off), or 1 <= top_k <= max_top_k.  With top_k <= 64 (and not the
+ *       dot-product path) the top-k is fused: the streaming pass keeps, per
+ *       batch row, vocabulary tile and wave, the 4 best scores it saw and a
+ *       bound on the scores it dropped; a second launch per batch chunk
+ *       selects the row's top k from those lists, rescoring a tile from H and
+ *       W when its bound reaches the k-th score, and draws the Gumbel-max
+ *       among them.  No [B, V] scores reach HBM.  Larger k stores each
+ *       chunk's fp32 scores in the context's workspace (max_top_k > 64 at
+ *       fs_create) and selects from them.
  * Requires 1 <= B <= max_B, 8 <= d, d % 8 == 0, 1 <= V <= max_V < 2^31. */
 int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
                    int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
                    const uint32_t* mask, int64_t ldm, int top_k, int32_t* out_idx, float* tile_max,
                    int32_t* tile_arg, int path);
+
+/* Top-k, then top-p (nucleus) sampling, fused.
+ *   The top_k largest scores s of the row's allowed ids are kept as in
+ *   fs_fmms_sample; sorted by s (descending, lower id first), a kept id stays
+ *   in the nucleus while the weight exp(s - s_max) of the ids ahead of it,
+ *   summed in fp64, is below top_p times the weight of all kept ids -- the
+ *   shortest prefix holding top_p of their mass.  out_idx[b] is the Gumbel-max
+ *   over the nucleus with the same per-id noise (-1 if no id is allowed).
+ *   top_p = 1 gives fs_fmms_sample's top-k sample.
+ *   [nucleus sampling as defined by Holtzman et al., "The Curious Case of
+ *    Neural Text Degeneration", ICLR 2020; cjcn.com.cn and news.neo-ai.one
+ *    FlashSampling articles: the method is compatible with top-p sampling]
+ * Requires 1 <= top_k <= min(max_top_k, 64) (FS_ERR_UNSUPPORTED above 64),
+ * 0 < top_p <= 1, path FS_PATH_AUTO or FS_PATH_MFMA; other arguments as in
+ * fs_fmms_sample. */
+int fs_fmms_sample_top_p(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                         int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                         const uint32_t* mask, int64_t ldm, int top_k, float top_p, int32_t* out_idx, int path);
 
 /* Several samples per row from one pass over W.
  *   out_idx [B, num_samples] int32 (row-major): out_idx[b * num_samples + s] is

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     fs_fmms_sample,
     fs_fmms_sample_multi,
     fs_fmms_sample_noalloc,
+    fs_fmms_sample_top_p,
     fs_fmms_tiling,
     fs_group_combine,
     fs_group_summaries,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "fs_last_error": (ctypes.c_char_p, []),
     "fs_fmms_tiling": (_I, [_P, _I, _I, _I64, _I, ctypes.POINTER(_I64), _P]),
     "fs_fmms_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _P, _I]),
+    "fs_fmms_sample_top_p": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _F, _P, _I]),
     "fs_fmms_sample_multi": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _I]),
     "fs_unfused_sample": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _I, _P, _P, _I64,
                                _I]),
@@ -184,6 +185,24 @@ def fs_fmms_sample(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: floa
     _check(_lib.fs_fmms_sample(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
                                float(temperature), seed, step, mptr, ldm, top_k, out.data_ptr(), _dptr(tile_max),
                                _dptr(tile_arg), path))
+    return out
+
+
+def fs_fmms_sample_top_p(ctx: int, H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+                         top_k: int, top_p: float, mask: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                         path: int = FS_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Top-k, then the nucleus holding top_p of the kept mass; returns out [B] int32."""
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=H.device)
+    _device_buffer(out, torch.int32, B, "out")
+    mptr, ldm = _mask_args(mask, B, V)
+    _check(_lib.fs_fmms_sample_top_p(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, V,
+                                     float(temperature), seed, step, mptr, ldm, top_k, float(top_p), out.data_ptr(),
+                                     path))
     return out
 
 

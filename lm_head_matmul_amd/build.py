@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in ("fs_api.hip", "fs_kernels.hip", "fs_stream_flat.hip",
-                                           "fs_stream_group.hip", "fs_stream_store.hip")]
+                                           "fs_stream_group.hip", "fs_stream_store.hip",
+                                           "fs_stream_topk.hip")]
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libflashsampling.so")
 

@@ -26,7 +26,11 @@ struct fs_ctx {
   float* ws_m;
   float* ws_s;
   void* base;
-  // top-k: fp32 scores of up to topk_rows batch rows, [topk_rows][topk_ldl]
+  // fused top-k: per (row, tile, wave) candidate lists of up to topk_rows rows
+  uint64_t* topk_lists;
+  // top-k from stored scores (k above kTopkFusedMax, the dot path, and the
+  // unfused comparator): fp32 scores of up to topk_rows batch rows,
+  // [topk_rows][topk_ldl] (allocated when max_top_k > kTopkFusedMax)
   float* topk_ws;
   int64_t topk_ldl;
   int topk_rows;
@@ -167,6 +171,7 @@ void fill_common(fsk::StreamParams& p, const fs_ctx* ctx, const uint16_t* H, int
   p.ws_idx = ctx->ws_idx;
   p.ws_m = ctx->ws_m;
   p.ws_s = ctx->ws_s;
+  p.top_p = 1.0f;
 }
 
 // Launches the streaming kernel over the batch in chunks of at most
@@ -312,6 +317,26 @@ int noalloc_setup(int dev, NoAllocDevice& out) {
   return FS_OK;
 }
 
+// Fused top-k (and its nucleus): the streaming pass keeps short candidate
+// lists per (row, tile, wave) instead of the scores, and a merge launch per
+// batch chunk selects the top k, cuts the nucleus when top_p < 1, and samples.
+int sample_topk_fused(fs_ctx* ctx, hipStream_t stream, const uint16_t* H, int64_t ldh, const uint16_t* W,
+                      int64_t ldw, int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                      const uint32_t* mask, int64_t ldm, int top_k, float top_p, int32_t* out_idx, int path) {
+  fsk::StreamParams p;
+  fill_common(p, ctx, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm);
+  p.top_k = top_k;
+  p.top_p = top_p;
+  p.topk_cand = ctx->topk_lists;
+  return run_stream_chunks(
+      ctx, p, path, fsk::EPI_TOPK, stream,
+      [&](fsk::StreamParams& c, int r0) {
+        c.out_idx = out_idx + r0;
+        c.tile_ratio = mask ? 0 : fsk::kXcdTileRatio;
+      },
+      ctx->topk_rows);
+}
+
 }  // namespace
 
 extern "C" {
@@ -341,7 +366,8 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     delete c;
     return hip_fail(e, "hipDeviceGetAttribute");
   }
-  c->max_tiles = c->n_cu;
+  // one vocabulary tile per CU; the fused top-k's merge holds a tile per thread
+  c->max_tiles = c->n_cu < fsk::kTopkMergeThreads ? c->n_cu : fsk::kTopkMergeThreads;
   {  // the allocation-free entry point's scratch address on this device, looked up at set-up
     NoAllocDevice nd;
     const int rc = noalloc_setup(device, nd);
@@ -378,8 +404,12 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
   if (max_top_k > 0) {
     c->topk_rows = max_B < fsk::kMfmaMaxB ? max_B : fsk::kMfmaMaxB;
     c->topk_ldl = (max_V + 3) / 4 * 4;
-    e = hipMalloc(&c->topk_ws, (size_t)c->topk_rows * (size_t)c->topk_ldl * sizeof(float));
+    const size_t lists = (size_t)c->topk_rows * c->max_tiles * fsk::kWaves * fsk::kTopkSlot * sizeof(uint64_t);
+    e = hipMalloc(&c->topk_lists, lists);
+    if (e == hipSuccess && max_top_k > fsk::kTopkFusedMax)
+      e = hipMalloc(&c->topk_ws, (size_t)c->topk_rows * (size_t)c->topk_ldl * sizeof(float));
     if (e != hipSuccess) {
+      if (c->topk_lists) (void)hipFree(c->topk_lists);
       (void)hipFree(c->cdf_ws);
       (void)hipFree(c->base);
       delete c;
@@ -396,7 +426,8 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
       if (c->topk_sel) (void)hipFree(c->topk_sel);
-      (void)hipFree(c->topk_ws);
+      if (c->topk_ws) (void)hipFree(c->topk_ws);
+      (void)hipFree(c->topk_lists);
       (void)hipFree(c->cdf_ws);
       (void)hipFree(c->base);
       delete c;
@@ -420,6 +451,7 @@ void fs_destroy(fs_ctx* ctx) {
   DeviceGuard guard(ctx->device);
   if (ctx->base) (void)hipFree(ctx->base);
   if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
+  if (ctx->topk_lists) (void)hipFree(ctx->topk_lists);
   if (ctx->topk_sel) (void)hipFree(ctx->topk_sel);
   if (ctx->cdf_ws) (void)hipFree(ctx->cdf_ws);
   delete ctx;
@@ -456,10 +488,17 @@ int fs_fmms_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, co
   DeviceGuard guard(ctx->device);
   if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
   fsk::StreamParams p;
+  if (top_k > 0 && top_k <= fsk::kTopkFusedMax && path != FS_PATH_DOT)
+    return sample_topk_fused(ctx, (hipStream_t)stream, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm,
+                             top_k, 1.0f, out_idx, path);
   if (top_k > 0) {
-    // The exact top-k boundary of a row needs all of its scores: the streaming
-    // pass stores them into the context's workspace (batch chunks of
-    // topk_rows rows) and the selection launches sample the kept set.
+    // Larger k, or the dot-product path: the exact top-k boundary of a row is
+    // found from all of its scores, which the streaming pass stores into the
+    // context's workspace (batch chunks of topk_rows rows); the selection
+    // launches sample the kept set.
+    if (!ctx->topk_ws)
+      return fail(FS_ERR_CAPACITY, "top_k=%d on this path needs a context created with max_top_k > %d", top_k,
+                  fsk::kTopkFusedMax);
     hipStream_t s = (hipStream_t)stream;
     for (int r0 = 0; r0 < B; r0 += ctx->topk_rows) {
       const int Bc = (B - r0) < ctx->topk_rows ? (B - r0) : ctx->topk_rows;
@@ -513,6 +552,28 @@ int fs_fmms_sample_multi(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t l
         c.tile_ratio = fsk::kXcdTileRatio;
       },
       ctx->max_B);
+}
+
+int fs_fmms_sample_top_p(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W,
+                         int64_t ldw, int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,
+                         const uint32_t* mask, int64_t ldm, int top_k, float top_p, int32_t* out_idx, int path) {
+  int rc = check_operands(ctx, H, ldh, W, ldw, B, d, V, temperature, mask, ldm, V);
+  if (rc != FS_OK) return rc;
+  if (!out_idx) return fail(FS_ERR_INVALID_ARG, "out_idx is NULL");
+  if (top_k < 1 || top_k > ctx->max_top_k)
+    return fail(top_k < 1 ? FS_ERR_INVALID_ARG : FS_ERR_CAPACITY, "top_k=%d outside [1, max_top_k=%d]", top_k,
+                ctx->max_top_k);
+  if (top_k > fsk::kTopkFusedMax)
+    return fail(FS_ERR_UNSUPPORTED, "top-p runs on the fused top-k candidates: top_k=%d above %d", top_k,
+                fsk::kTopkFusedMax);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(FS_ERR_INVALID_ARG, "top_p=%g outside (0, 1]", (double)top_p);
+  if (path != FS_PATH_AUTO && path != FS_PATH_MFMA)
+    return fail(path == FS_PATH_DOT ? FS_ERR_UNSUPPORTED : FS_ERR_INVALID_ARG, "path %d: top-p runs on the MFMA kernels",
+                path);
+  DeviceGuard guard(ctx->device);
+  if (!guard.ok) return fail(FS_ERR_HIP, "cannot make device %d current", ctx->device);
+  return sample_topk_fused(ctx, (hipStream_t)stream, H, ldh, W, ldw, B, d, V, temperature, seed, step, mask, ldm,
+                           top_k, top_p, out_idx, path);
 }
 
 int fs_unfused_sample(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,

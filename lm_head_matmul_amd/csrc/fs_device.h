@@ -133,6 +133,29 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os
   m = mm;
 }
 
+// ---------------------------------------------------------------------------
+// Top-k keys: one 64-bit word per (score, id) whose unsigned order is the
+// selection order -- higher score first, lower id first among equal scores.
+// High word: the score's bits mapped to an unsigned order (sign flipped for
+// positives, all bits inverted for negatives; -0 folded onto +0); low word:
+// the id's complement.  0 marks an empty slot: every real key exceeds it.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_bits(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ uint64_t topk_key(float s, int32_t id) {
+  return ((uint64_t)order_bits(s) << 32) | (uint64_t)(~(uint32_t)id);
+}
+
+__device__ __forceinline__ float topk_key_score(uint64_t key) { return order_bits_inv((uint32_t)(key >> 32)); }
+__device__ __forceinline__ int32_t topk_key_id(uint64_t key) { return (int32_t)(~(uint32_t)key); }
+
 __device__ __forceinline__ bool mask_allows(const uint32_t* __restrict__ mask_row, int64_t gv) {
   return (mask_row[gv >> 5] >> (uint32_t)(gv & 31)) & 1u;
 }

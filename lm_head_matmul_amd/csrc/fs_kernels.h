@@ -6,7 +6,10 @@
 
 namespace fsk {
 
-enum Epilogue { EPI_FLAT = 0, EPI_GROUP = 1, EPI_STORE = 2 };
+// EPI_TOPK: the fused top-k pass -- per lane, a short list of the best scores
+// it saw; per (row, tile, wave) a merged list and a bound on what it dropped
+// (see fs_stream.h), finished by topk_merge_kernel.
+enum Epilogue { EPI_FLAT = 0, EPI_GROUP = 1, EPI_STORE = 2, EPI_TOPK = 3 };
 
 struct GroupSummary {  // same layout as fs_group_summary_t
   float lse;
@@ -65,6 +68,11 @@ struct StreamParams {
   float* logits;  // EPI_STORE: [B][ldl] fp32
   int64_t ldl;
   int tile_ratio;  // 0: equal tiles; else XCD-weighted tiles (see tile_lo)
+  // EPI_TOPK: k, and the per-(row, tile, wave) candidate lists, laid out as
+  // topk_cand[((b * kWaves + wave) * kTopkSlot + j) * n_tiles + tile]
+  int top_k;
+  uint64_t* topk_cand;
+  float top_p;  // EPI_TOPK: nucleus of the kept ids (1: all of them)
 };
 
 struct SampleParams {  // unfused second pass: sample from stored logits
@@ -158,6 +166,8 @@ constexpr int kLayoutTable = 0;     // round-major kernel with the tile's noise 
 constexpr int kLayoutEpilogue = 1;  // round-major kernel, noise in the epilogue
 constexpr int kLayoutStore = 0;     // round-major kernel storing the logits
 constexpr int kLayoutKouter = 1;    // chunk-outer kernel
+constexpr int kLayoutTopk = 0;      // round-major kernel with the top-k epilogue
+constexpr int kLayoutKouterTopk = 1;  // chunk-outer kernel with the top-k epilogue
 constexpr int kLayoutDot = 0;       // dot-product kernel
 // Rounds per pass of the chunk-outer kernel (accumulator sets a wave keeps in
 // registers), by epilogue, batch blocks and masking: the most that fit 256
@@ -165,8 +175,18 @@ constexpr int kLayoutDot = 0;       // dot-product kernel
 // five rounds (one pass over the decode heads' tiles, 8 VGPRs spilled outside
 // the chunk loop) measured faster than three.
 constexpr int kouter_max_rounds(int epi, int nb, bool masked) {
-  return (nb <= 2 || epi == EPI_STORE || (epi == EPI_FLAT && !masked)) ? 5 : 3;
+  return (nb <= 2 || epi == EPI_STORE || ((epi == EPI_FLAT || epi == EPI_TOPK) && !masked)) ? 5 : 3;
 }
+// Fused top-k: each lane keeps its kTopkLane best (score, id) pairs; each wave
+// merges its lanes' lists per batch row into kTopkLane entries plus one bound
+// (kTopkSlot = kTopkLane + 1 words of the candidate buffer).  k up to
+// kTopkFusedMax runs fused; larger k stores the logits and selects from them.
+constexpr int kTopkLane = 4;
+constexpr int kTopkSlot = kTopkLane + 1;
+constexpr int kTopkFusedMax = 64;
+constexpr int kTopkMergeThreads = 256;
+constexpr int kTopkMergeCap = 4096;      // candidate keys a row's merge holds in LDS
+constexpr int kTopkMergeMaxTiles = 1024;
 constexpr int kMaskLdsMax = 16 * 1024;  // LDS bytes for the staged tile mask
 
 // First 16-row block of tile t of n_tiles over n_mblocks blocks.  ratio == 0:
@@ -203,6 +223,7 @@ hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi
 template <int EPI>
 hipError_t launch_stream_epi(const StreamParams& p, const StreamConfig& cfg, hipStream_t stream);
 hipError_t launch_sample_logits(const SampleParams& p, hipStream_t stream);
+hipError_t launch_topk_merge(const StreamParams& p, hipStream_t stream);
 hipError_t launch_topk_sample(const TopkParams& p, hipStream_t stream);
 hipError_t launch_cdf_sample(const CdfParams& p, hipStream_t stream);
 hipError_t launch_group_combine(const GroupSummary* s, int n_groups, int B, uint64_t seed, uint64_t step, int mode,

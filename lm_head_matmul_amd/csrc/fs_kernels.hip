@@ -9,6 +9,7 @@ namespace fsk {
 extern template hipError_t launch_stream_epi<EPI_FLAT>(const StreamParams&, const StreamConfig&, hipStream_t);
 extern template hipError_t launch_stream_epi<EPI_GROUP>(const StreamParams&, const StreamConfig&, hipStream_t);
 extern template hipError_t launch_stream_epi<EPI_STORE>(const StreamParams&, const StreamConfig&, hipStream_t);
+extern template hipError_t launch_stream_epi<EPI_TOPK>(const StreamParams&, const StreamConfig&, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Unfused second pass: sample from fp32 logits stored in HBM.  Tile t covers a
@@ -555,6 +556,403 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams
   topk_finish_row(p, row, b, keep_all, above, inbin, sh);
 }
 // ---------------------------------------------------------------------------
+// Fused top-k, second launch: one workgroup per batch row merges the lists the
+// streaming pass (EPI_TOPK) left per (tile, wave): kTopkLane keys and a bound
+// on the keys that wave dropped.  [readus.org FlashSampling summary, section on
+// Top-K and masking: a pre-filter keeps candidates, exact Gumbel-Max runs on
+// them]  Keys order (score desc, id asc); the row's top-k is the k largest.
+//   1. theta = the k-th largest tile maximum.  k distinct ids reach it, so the
+//      row's k-th key tau is at least theta, and only list entries >= theta can
+//      be kept: they are gathered (at most 32 k of them).
+//   2. tau = the k-th largest gathered key (0 = keep all if there are fewer).
+//   3. A wave whose bound reaches tau may have dropped a kept id.  Then its
+//      tile is rescored (every id of the tile recomputed from H and W in fp32)
+//      and the selection redone over the other tiles' lists and the rescored
+//      ids, with the threshold lowered by the near-tie margin so that another
+//      fp32 summation order cannot push one of the k tile maxima under it;
+//      repeated until no unrescored tile's bound reaches tau.  On the decode
+//      workloads no bound comes near tau; ties and tiny vocabularies take it.
+//   4. Gumbel-max over the kept ids with the per-id noise of the plain sampler.
+// Thread t holds tile t's lists (n_tiles <= kTopkMergeThreads).
+// ---------------------------------------------------------------------------
+static_assert(kTopkMergeThreads == 256 && kTopkMergeCap % kTopkMergeThreads == 0, "merge geometry");
+static_assert(kTopkFusedMax <= 64, "the nucleus cut sorts the kept keys within one wave");
+
+// Wave-wide bitonic sort, descending, of one 64-bit key per lane.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const uint64_t o = __shfl_xor(x, j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
+      x = keep_max ? (x > o ? x : o) : (x < o ? x : o);
+    }
+  }
+  return x;
+}
+
+struct TopkMergeShared {
+  alignas(16) uint64_t F[kTopkMergeCap];  // gathered keys
+  uint16_t Ft[kTopkMergeCap];  // tile of each gathered key
+  alignas(16) uint64_t S[kTopkMergeThreads];
+  uint64_t Tw[kTopkMergeThreads / 64];
+  int rescored[kTopkMergeThreads];
+  int nF, nnew;
+  uint64_t theta, tau;
+  float red_v[kTopkMergeThreads / 64];
+  int32_t red_i[kTopkMergeThreads / 64];
+};
+
+// Rank of one key per thread (0: none) among the block's keys: the waves sort
+// their keys, then each key's rank is its lane plus, for every other wave, the
+// count of that wave's keys above it (binary search).  On return x is the key
+// the thread now holds.  Non-zero keys are distinct.
+__device__ __forceinline__ int block_rank(uint64_t& x, TopkMergeShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_sort_desc(x);
+  sh.S[threadIdx.x] = x;
+  __syncthreads();
+  int r = lane;
+  for (int w = 0; w < kTopkMergeThreads / 64; ++w) {
+    if (w == wave) continue;
+    const uint64_t* L = sh.S + w * 64;
+    int lo = 0, hi = 64;  // first entry of the descending list L that is not above x
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L[mid] > x)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    r += lo;
+  }
+  __syncthreads();
+  return r;
+}
+
+// Count of the n keys of F (LDS, 16-byte aligned) above x: every thread reads
+// the same words, 8 keys per batch of loads so that their latency overlaps.
+__device__ __forceinline__ int rank_in(const uint64_t* F, int n, uint64_t x) {
+  int r = 0, j = 0;
+  for (; j + 8 <= n; j += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = F[j + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += v[u] > x ? 1 : 0;
+  }
+  for (; j < n; ++j) r += F[j] > x ? 1 : 0;
+  return r;
+}
+
+// The k-th largest of the gathered keys, 0 if there are fewer than k.
+__device__ uint64_t topk_select_kth(TopkMergeShared& sh, int k) {
+  __syncthreads();
+  const int n = sh.nF;
+  if (threadIdx.x == 0) sh.tau = 0;
+  if (n <= kTopkMergeThreads) {
+    uint64_t x = (int)threadIdx.x < n ? sh.F[threadIdx.x] : 0ull;
+    const int r = block_rank(x, sh);  // its first barrier orders the store to tau above
+    if (x != 0 && r == k - 1) sh.tau = x;
+  } else {
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kTopkMergeThreads) {
+      const uint64_t x = sh.F[i];
+      if (rank_in(sh.F, n, x) == k - 1) sh.tau = x;
+    }
+  }
+  __syncthreads();
+  return sh.tau;
+}
+
+// Keeps the k largest gathered keys (moved to the front).
+__device__ __noinline__ void topk_compact(TopkMergeShared& sh, int k) {
+  constexpr int kPer = kTopkMergeCap / kTopkMergeThreads;
+  __syncthreads();
+  const int n = sh.nF;
+  uint64_t key[kPer];
+  int rank[kPer];
+  uint16_t tile[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = threadIdx.x + q * kTopkMergeThreads;
+    key[q] = i < n ? sh.F[i] : 0ull;
+    tile[q] = i < n ? sh.Ft[i] : (uint16_t)0;
+    rank[q] = key[q] != 0 ? rank_in(sh.F, n, key[q]) : INT32_MAX;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kPer; ++q)
+    if (rank[q] < k) {
+      sh.F[rank[q]] = key[q];
+      sh.Ft[rank[q]] = tile[q];
+    }
+  __syncthreads();
+  if (threadIdx.x == 0) sh.nF = n < k ? n : k;
+  __syncthreads();
+}
+
+// Block-wide append of one key per thread (0: none); compacts first when a
+// full round might not fit.  Every thread of the block calls it.
+__device__ __forceinline__ void topk_append(TopkMergeShared& sh, uint64_t key, int tile, int k) {
+  __syncthreads();
+  if (sh.nF + kTopkMergeThreads > kTopkMergeCap) topk_compact(sh, k);
+  if (key != 0) {
+    const int i = atomicAdd(&sh.nF, 1);
+    sh.F[i] = key;
+    sh.Ft[i] = (uint16_t)tile;
+  }
+}
+
+// Score of vocab row v (local to the launch) for batch row b, recomputed in fp32.
+__device__ float topk_rescore(const StreamParams& p, int b, int v) {
+  const uint16_t* h = p.H + (int64_t)b * p.ldh;
+  const uint16_t* w = p.W + (int64_t)v * p.ldw;
+  float acc = 0.0f;
+  for (int k = 0; k < p.d; k += 8) {
+    const u32x4_t hv = *(const u32x4_t*)(h + k);
+    const u32x4_t wv = *(const u32x4_t*)(w + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_fmaf(__uint_as_float(hv[i] << 16), __uint_as_float(wv[i] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(hv[i] & 0xFFFF0000u), __uint_as_float(wv[i] & 0xFFFF0000u), acc);
+    }
+  }
+  return acc * p.inv_t;
+}
+
+__global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const StreamParams p) {
+  __shared__ TopkMergeShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+  const int nt = p.n_tiles, k = p.top_k;
+  const bool has = tid < nt;
+  const uint64_t* cand = p.topk_cand + (int64_t)b * kWaves * kTopkSlot * nt;
+  const uint32_t row = (uint32_t)(p.row_offset + b);
+  auto noise_of = [&](int32_t id) {
+    const Philox4 rr = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)id >> 2, row, p.step_lo, p.step_hi);
+    const uint32_t q = (uint32_t)id & 3u;
+    return gumbel_from_bits(q == 0 ? rr.w[0] : q == 1 ? rr.w[1] : q == 2 ? rr.w[2] : rr.w[3]);
+  };
+  uint64_t e[kWaves][kTopkLane], hb[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+    for (int j = 0; j < kTopkLane; ++j) e[w][j] = has ? cand[(int64_t)(w * kTopkSlot + j) * nt + tid] : 0ull;
+    hb[w] = has ? cand[(int64_t)(w * kTopkSlot + kTopkLane) * nt + tid] : 0ull;
+  }
+  // 1. theta, a lower bound of the row's k-th key: each wave sorts its 64
+  // tile maxima, and the smallest of the four waves' ceil(k/4)-th largest has at
+  // least k keys at or above it.  If a wave holds fewer keys than that, or the
+  // bound gathers more than 32 k entries, theta is the k-th largest tile
+  // maximum itself (ranks by counting over LDS).
+  uint64_t x = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) x = e[w][0] > x ? e[w][0] : x;
+  sh.S[tid] = x;
+  sh.rescored[tid] = 0;
+  if (tid == 0) {
+    sh.theta = 0;
+    sh.nF = 0;
+    sh.nnew = 0;
+  }
+  {
+    const uint64_t xs = wave_sort_desc(x);
+    const int kw = (k + kTopkMergeThreads / 64 - 1) / (kTopkMergeThreads / 64);
+    if (lane == kw - 1) sh.Tw[wave] = xs;
+  }
+  __syncthreads();
+  uint64_t th = ~0ull;
+#pragma unroll
+  for (int w = 0; w < kTopkMergeThreads / 64; ++w) th = sh.Tw[w] < th ? sh.Tw[w] : th;
+  int cnt = 0;
+  if (th != 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j) cnt += e[w][j] >= th ? 1 : 0;
+    atomicAdd(&sh.nF, cnt);
+  }
+  __syncthreads();
+  uint64_t theta = th;
+  if (th == 0 || sh.nF > 32 * k) {
+    if (x != 0 && rank_in(sh.S, nt, x) == k - 1) sh.theta = x;
+    __syncthreads();
+    theta = sh.theta;
+    th = theta != 0 ? theta : 1ull;  // fewer than k tiles hold a key: gather them all
+    cnt = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j) cnt += e[w][j] >= th ? 1 : 0;
+  }
+  __syncthreads();
+  if (tid == 0) sh.nF = 0;
+  __syncthreads();
+  int at = cnt > 0 ? atomicAdd(&sh.nF, cnt) : 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int j = 0; j < kTopkLane; ++j)
+      if (e[w][j] >= th) {
+        sh.F[at] = e[w][j];
+        sh.Ft[at] = (uint16_t)tid;
+        ++at;
+      }
+  __syncthreads();
+  // 2. tau: the k-th largest gathered key (0 if fewer than k); each gathered key
+  // knows its rank, so the kept ones (rank < k) are known too
+  const int n0 = sh.nF;
+  if (tid == 0) sh.tau = 0;
+  __syncthreads();
+  const uint64_t mykey = tid < n0 ? sh.F[tid] : 0ull;  // one gathered key per thread (n0 <= 32 k)
+  int myrank = INT32_MAX;
+  if (n0 <= kTopkMergeThreads) {
+    if (mykey != 0) myrank = rank_in(sh.F, n0, mykey);
+    if (myrank == k - 1) sh.tau = mykey;
+  } else {
+    for (int i = tid; i < n0; i += kTopkMergeThreads)
+      if (rank_in(sh.F, n0, sh.F[i]) == k - 1) sh.tau = sh.F[i];
+  }
+  // 3. a tile whose dropped keys could reach tau is rescored
+  __syncthreads();
+  uint64_t tau = sh.tau;
+  bool flag = false;
+  if (has)
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) flag |= hb[w] != 0 && hb[w] >= tau;
+  if (flag) {
+    sh.rescored[tid] = 1;
+    atomicAdd(&sh.nnew, 1);
+  }
+  __syncthreads();
+  bool fast = sh.nnew == 0 && n0 <= kTopkMergeThreads;
+  if (sh.nnew != 0) {
+    // rebuild: the lists of the other tiles, every id of the rescored ones;
+    // repeated while the new tau brings more tiles in
+    const uint64_t th2 =
+        theta != 0 ? (uint64_t)order_bits(topk_key_score(theta) - 1e-3f * (1.0f + fabsf(topk_key_score(theta)))) << 32
+                   : 1ull;
+    for (;;) {
+      __syncthreads();
+      if (tid == 0) sh.nF = 0;
+      const bool mine = has && !sh.rescored[tid];
+#pragma unroll 1
+      for (int q = 0; q < kWaves * kTopkLane; ++q) {  // this path reads the lists again from memory
+        const int w = q / kTopkLane, j = q - w * kTopkLane;
+        const uint64_t v = mine ? cand[(int64_t)(w * kTopkSlot + j) * nt + tid] : 0ull;
+        topk_append(sh, v >= th2 ? v : 0ull, tid, k);
+      }
+#pragma unroll 1
+      for (int t = 0; t < nt; ++t) {
+        if (!sh.rescored[t]) continue;  // uniform: written before the last barrier
+        const int64_t lo = tile_lo(t, p.n_mblocks, p.n_tiles, p.tile_ratio) * 16;
+        int64_t hi = tile_lo(t + 1, p.n_mblocks, p.n_tiles, p.tile_ratio) * 16;
+        hi = hi < p.V ? hi : p.V;
+        const uint32_t* mrow = p.mask ? p.mask + (int64_t)(p.row_offset + b) * p.ldm : nullptr;
+#pragma unroll 1
+        for (int64_t v0 = lo; v0 < hi; v0 += kTopkMergeThreads) {
+          const int64_t v = v0 + tid;
+          uint64_t key = 0;
+          if (v < hi) {
+            const int gv = (int)(p.vocab_offset + v);
+            if (mrow == nullptr || mask_allows(mrow, gv)) {
+              const float sc = topk_rescore(p, b, (int)v);
+              if (sc == sc) key = topk_key(sc, gv);
+            }
+          }
+          topk_append(sh, key >= th2 ? key : 0ull, t, k);
+        }
+      }
+      tau = topk_select_kth(sh, k);
+      if (tid == 0) sh.nnew = 0;
+      __syncthreads();
+      flag = false;
+      if (has && !sh.rescored[tid])
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) flag |= hb[w] != 0 && hb[w] >= tau;
+      if (flag) {
+        sh.rescored[tid] = 1;
+        atomicAdd(&sh.nnew, 1);
+      }
+      __syncthreads();
+      if (sh.nnew == 0) break;
+    }
+  }
+  // 4. Gumbel-max over the kept keys (>= tau): all of them, or with top_p < 1
+  // the nucleus of the kept ids -- sorted by key, an id stays while the fp64
+  // weight exp(s - s_max) of the ids before it is below top_p times their total
+  // [nucleus sampling, Holtzman et al., ICLR 2020, over the top-k set]
+  const int n = sh.nF;
+  float bv = -INFINITY;
+  int32_t bi = -1;
+  if (p.top_p < 1.0f) {
+    // the kept keys (at most k <= 64) in order into S, then wave 0 cuts them
+    __syncthreads();
+    if (fast) {
+      if (myrank < k) sh.S[myrank] = mykey;
+    } else {
+      for (int i = tid; i < n; i += kTopkMergeThreads) {
+        const uint64_t key = sh.F[i];
+        if (key != 0 && key >= tau) sh.S[rank_in(sh.F, n, key)] = key;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int nk = n < k ? n : k;
+      const uint64_t key = lane < nk ? sh.S[lane] : 0ull;  // lane i: the i-th largest kept key
+      const double s0 = (double)topk_key_score(sh.S[0]);
+      const double w = key != 0 ? exp((double)topk_key_score(key) - s0) : 0.0;
+      double incl = w;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const double total = __shfl(incl, 63);
+      if (key != 0 && incl - w < (double)p.top_p * total) {
+        bi = topk_key_id(key);
+        bv = topk_key_score(key) + noise_of(bi);
+      }
+    }
+  } else if (fast) {
+    if (myrank < k) {
+      bi = topk_key_id(mykey);
+      bv = topk_key_score(mykey) + noise_of(bi);
+    }
+  } else {
+    for (int i = tid; i < n; i += kTopkMergeThreads) {
+      const uint64_t key = sh.F[i];
+      if (key == 0 || key < tau) continue;
+      const int32_t id = topk_key_id(key);
+      merge_best(bv, bi, topk_key_score(key) + noise_of(id), id);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int32_t oi = __shfl_xor(bi, off);
+    merge_best(bv, bi, ov, oi);
+  }
+  if (lane == 0) {
+    sh.red_v[wave] = bv;
+    sh.red_i[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 0; w < kTopkMergeThreads / 64; ++w) merge_best(bv, bi, sh.red_v[w], sh.red_i[w]);
+    p.out_idx[b] = bi;
+  }
+}
+
+hipError_t launch_topk_merge(const StreamParams& p, hipStream_t stream) {
+  if (p.n_tiles > kTopkMergeThreads || p.top_k < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(p.B), dim3(kTopkMergeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Conventional comparator, not the method: the softmax pipeline the fused
 // sampler replaces [readus.org FlashSampling summary, the essay part: the
 // softmax pipeline exponentiates every score, normalizes, and scans the
@@ -859,6 +1257,7 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     cfg.lds_bytes = 2 * (kWideMaxB + 1) * kWideRowBytes;  // also covers the final reduction's scratch
     return cfg.lds_bytes <= kLdsMax;
   }
+  if (epi == EPI_TOPK && (cfg.dot || p.n_tiles > kTopkMergeThreads)) return false;  // MFMA kernels only
   const int Bp = cfg.dot ? cfg.bd : cfg.nb * 16;
   const int hr = cfg.dot ? cfg.bd : (p.B < Bp ? p.B + 1 : Bp);
   p.h_rows = hr;
@@ -885,8 +1284,11 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   // a mask, d=5120, B=1 and 8: 265.1 and 268.7 us, against 260.5 and 261.0).
   // The stored-logits epilogue and the dot-product kernel use no table.
   const bool table_fits = (int64_t)hr * rowstride(p.nsub) + (int64_t)p.B * (tile_rows + 4) * 4 <= budget;
+  // The top-k epilogue runs no Philox in its loop and needs no table: resident
+  // H up to 16 rows without a mask.
   const bool prefer_resident =
-      epi == EPI_STORE || cfg.dot || (p.nsub <= 8 ? p.B <= 16 : table_fits && p.mask == nullptr);
+      epi == EPI_STORE || cfg.dot ||
+      (p.nsub <= 8 ? p.B <= 16 : (epi == EPI_TOPK ? p.B <= 16 : table_fits) && p.mask == nullptr);
   if ((int64_t)hr * rowstride(p.nsub) <= budget && prefer_resident) {
     p.cs = p.nsub;
     p.nchunk = 1;
@@ -940,7 +1342,8 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
     // keep the stored logits equal bit for bit to the fused path's), whole XCD
     // sets of tiles, at least 16 blocks a tile (with fewer, one more block can
     // add a round to a tile)
-    if (p.tile_ratio != 0 && !((epi == EPI_FLAT || epi == EPI_STORE) && p.mask == nullptr && p.group_tiles == 0 &&
+    if (p.tile_ratio != 0 && !((epi == EPI_FLAT || epi == EPI_STORE || epi == EPI_TOPK) && p.mask == nullptr &&
+                               p.group_tiles == 0 &&
                                p.n_tiles % 8 == 0 && p.n_mblocks >= 16 * (int64_t)p.n_tiles))
       p.tile_ratio = 0;
     int64_t max_blocks = 0;
@@ -960,7 +1363,7 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   // d <= 2048 the kernel running Philox in its epilogue, with its sub-blocks
   // rotated per workgroup, measured faster on MI355X (small decode B=1..16:
   // 118 -> 108 us); at d=4096 the table kernel is faster (195 vs 204 us).
-  if (!cfg.dot && cfg.fast && cfg.rm == 0 && epi != EPI_STORE && p.nsub > 8) {
+  if (!cfg.dot && cfg.fast && cfg.rm == 0 && (epi == EPI_FLAT || epi == EPI_GROUP) && p.nsub > 8) {
     const int pitch = (int)tile_rows + 4;
     const int64_t nbytes = (int64_t)p.B * pitch * 4;
     if (total + nbytes <= kLdsMax) {
@@ -1004,6 +1407,11 @@ hipError_t launch_stream(const StreamParams& p, const StreamConfig& cfg, int epi
       e = launch_stream_epi<EPI_STORE>(p, cfg, stream);
       if (e != hipSuccess) return e;
       return ev_after ? hipEventRecord(ev_after, stream) : hipSuccess;
+    case EPI_TOPK:
+      e = launch_stream_epi<EPI_TOPK>(p, cfg, stream);
+      if (e != hipSuccess) return e;
+      if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
+      return launch_topk_merge(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -386,6 +386,112 @@ __device__ __forceinline__ void epilogue_quad(const StreamParams& p, int v0, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused top-k epilogue.  [readus.org FlashSampling summary, section on Top-K
+// and masking: a pre-filter keeps a candidate set, then exact Gumbel-Max runs
+// inside it]  The exact top-k of a row is contained in the union of every
+// part's own top-k, for any partition of the vocabulary; a part that keeps
+// fewer entries is still exact as long as everything it dropped ranks below
+// the row's k-th kept score.  So each lane keeps its kTopkLane best (score,
+// id) pairs and counts what it saw; a wave merges its lanes' lists per
+// batch row into kTopkLane entries plus a bound on every dropped key, which
+// the merge kernel checks against the row's k-th key (and recomputes the
+// tile's ids where the check fails).
+// ---------------------------------------------------------------------------
+struct TopkList {
+  float s[kTopkLane];  // descending; -inf marks an empty entry
+  int32_t id[kTopkLane];
+  int seen;  // ids pushed: more than kTopkLane means some were dropped
+};
+
+__device__ __forceinline__ void topk_init(TopkList& t) {
+#pragma unroll
+  for (int j = 0; j < kTopkLane; ++j) {
+    t.s[j] = -INFINITY;
+    t.id[j] = -1;
+  }
+  t.seen = 0;
+}
+
+// Inserts (s, id).  A lane meets its ids in increasing order, so a strict
+// comparison keeps the lower id of two equal scores first, and anything it
+// drops ranks below its last entry.  NaN never enters (and counts as seen).
+__device__ __forceinline__ void topk_push(TopkList& t, float s, int32_t id) {
+  static_assert(kTopkLane == 4, "the insertion below is written for four entries");
+  const bool c0 = s > t.s[0], c1 = s > t.s[1], c2 = s > t.s[2], c3 = s > t.s[3];
+  ++t.seen;
+  t.s[3] = c2 ? t.s[2] : (c3 ? s : t.s[3]);
+  t.id[3] = c2 ? t.id[2] : (c3 ? id : t.id[3]);
+  t.s[2] = c1 ? t.s[1] : (c2 ? s : t.s[2]);
+  t.id[2] = c1 ? t.id[1] : (c2 ? id : t.id[2]);
+  t.s[1] = c0 ? t.s[0] : (c1 ? s : t.s[1]);
+  t.id[1] = c0 ? t.id[0] : (c1 ? id : t.id[1]);
+  t.s[0] = c0 ? s : t.s[0];
+  t.id[0] = c0 ? id : t.id[0];
+}
+
+__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t u64_min(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// End of a top-k streaming kernel: per batch column, merge the four lane
+// groups' lists of a wave (lanes l16, l16 + 16, l16 + 32, l16 + 48) and write
+// the wave's kTopkLane best keys and its bound -- the largest key it may have
+// dropped (0 if none) -- to the candidate buffer.  Two sorted lists of four
+// merge by one step of a bitonic merge: the elementwise maxima of one list and
+// the other reversed are the best four, the minima the four dropped.
+template <int NB>
+__device__ __forceinline__ void finish_wave_topk(const StreamParams& p, TopkList (&tk)[NB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    uint64_t k[kTopkLane];
+#pragma unroll
+    for (int j = 0; j < kTopkLane; ++j) k[j] = tk[nb].id[j] >= 0 ? topk_key(tk[nb].s[j], tk[nb].id[j]) : 0ull;
+    // whatever the lane dropped ranks below its last entry (keys are distinct)
+    uint64_t h = tk[nb].seen > kTopkLane && k[kTopkLane - 1] != 0 ? k[kTopkLane - 1] - 1 : 0ull;
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      uint64_t q[kTopkLane];
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j) q[j] = __shfl_xor(k[j], off);
+      h = u64_max(h, __shfl_xor(h, off));
+      uint64_t top[kTopkLane];
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j) {
+        top[j] = u64_max(k[j], q[kTopkLane - 1 - j]);
+        h = u64_max(h, u64_min(k[j], q[kTopkLane - 1 - j]));
+      }
+      // top is bitonic: two compare-exchange stages sort it descending
+      uint64_t a0 = u64_max(top[0], top[2]), a2 = u64_min(top[0], top[2]);
+      uint64_t a1 = u64_max(top[1], top[3]), a3 = u64_min(top[1], top[3]);
+      k[0] = u64_max(a0, a1);
+      k[1] = u64_min(a0, a1);
+      k[2] = u64_max(a2, a3);
+      k[3] = u64_min(a2, a3);
+    }
+    const int b = nb * 16 + l16;
+    if (grp == 0 && b < p.B) {
+      uint64_t* dst = p.topk_cand + ((int64_t)(b * kWaves + wave) * kTopkSlot) * p.n_tiles + blockIdx.x;
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j) dst[(int64_t)j * p.n_tiles] = k[j];
+      dst[(int64_t)kTopkLane * p.n_tiles] = h;
+    }
+  }
+}
+
+// Top-k epilogue of four consecutive ids v0 .. v0+3 (local ids) of one batch
+// row: the allowed, in-range ones enter the lane's list.
+__device__ __forceinline__ void topk_quad(const StreamParams& p, int v0, const float (&acc)[4], uint32_t bits,
+                                          TopkList& t) {
+  const int gv0 = (int)p.vocab_offset + v0;
+  const int rem = (int)p.V - v0;
+  const uint32_t ok4 = bits & (rem >= 4 ? 0xFu : (rem <= 0 ? 0u : (1u << rem) - 1u));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((ok4 >> i) & 1u) topk_push(t, acc[i] * p.inv_t, gv0 + i);
+}
+
 // Lane's W row pointer for vocab block `mb` (rows past the tile or past V are
 // clamped to the tile's last row; their results are never used).
 __device__ __forceinline__ const uint16_t* w_row(const StreamParams& p, const TileRange& tr, int64_t mb, int l16) {
@@ -792,7 +898,10 @@ __device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned
 template <int NB, int EPI, bool RESIDENT, bool FAST, bool MASKED, bool NOISE_LDS,
           int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams p) {
-  constexpr int LAYOUT = EPI == EPI_STORE ? kLayoutStore : NOISE_LDS ? kLayoutTable : kLayoutEpilogue;
+  constexpr int LAYOUT = EPI == EPI_STORE  ? kLayoutStore
+                         : EPI == EPI_TOPK ? kLayoutTopk
+                         : NOISE_LDS       ? kLayoutTable
+                                           : kLayoutEpilogue;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -829,6 +938,9 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     pend[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  TopkList tk[NB];  // EPI_TOPK only
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) topk_init(tk[nb]);
 
   // One sub-block: 8 k-steps; the B operands of step j + 1 are read from LDS
   // while the MFMAs of step j run.  (Left to itself the compiler waits on each
@@ -874,6 +986,8 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
         for (int i = 0; i < 4; ++i)
           if (v0 + i < p.V) dst[i] = a4[i];
       }
+    } else if (EPI == EPI_TOPK) {
+      topk_quad(p, (int)v0, a4, mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b), tk[nb]);
     } else {
       const uint32_t bits = mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
       f32x4_t g;
@@ -915,6 +1029,8 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   };
 
   int64_t last_blk;
+  // blocks on demand with H resident (the top-k merge rescores whole tiles, so
+  // it does not need to know which wave took which block)
   if constexpr (RESIDENT && FAST) {
     __shared__ int next_blk;
     last_blk = stream_driver_dynamic<RING, LAYOUT>(p, tr, smem, &next_blk, body_b, block_end, pre);
@@ -933,7 +1049,10 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
     for (int nb = 0; nb < NB; ++nb) finish_nb(last_blk, nb);
   }
   if (EPI == EPI_STORE) return;
-
+  if (EPI == EPI_TOPK) {
+    finish_wave_topk<NB>(p, tk);
+    return;
+  }
   finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
 }
 
@@ -954,7 +1073,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 // ---------------------------------------------------------------------------
 template <int NB, int EPI, bool MASKED, int RM>
 __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParams p) {
-  constexpr int LAYOUT = kLayoutKouter;
+  constexpr int LAYOUT = EPI == EPI_TOPK ? kLayoutKouterTopk : kLayoutKouter;
   static_assert(kFastRingChunked == 2, "two sub-blocks per chunk, two register buffers");
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -986,6 +1105,9 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
   for (int r = 0; r < RM; ++r)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  TopkList tk[NB];  // EPI_TOPK only
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) topk_init(tk[nb]);
 
   const int nchunk = p.nchunk;
   const int npass = (tr.rounds + RM - 1) / RM;
@@ -1038,6 +1160,9 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
           for (int i = 0; i < 4; ++i)
             if (v0 + i < p.V) dst[i] = a[nb][i];
         }
+      } else if (EPI == EPI_TOPK) {
+        const float a4[4] = {a[nb][0], a[nb][1], a[nb][2], a[nb][3]};
+        topk_quad(p, v0, a4, mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b), tk[nb]);
       } else {
         const float a4[4] = {a[nb][0], a[nb][1], a[nb][2], a[nb][3]};
         const uint32_t bits = mask_bits4<MASKED>(p, mask_lds, mw_lo, p.vocab_offset + v0, b);
@@ -1159,6 +1284,10 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
     }
   }
   if (EPI == EPI_STORE) return;
+  if (EPI == EPI_TOPK) {
+    finish_wave_topk<NB>(p, tk);
+    return;
+  }
   finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
 }
 
@@ -1519,6 +1648,7 @@ template <int EPI, bool RES, bool FAST, bool MK, bool NZ>
 static hipError_t launch_variant(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
   const int g = p.n_tiles, L = c.lds_bytes;
   if (c.dot) {
+    if constexpr (EPI == EPI_TOPK) return hipErrorInvalidValue;  // the top-k epilogue is MFMA-only
     switch (c.bd) {
       case 1: return launch_with_lds(fmms_dot_kernel<1, EPI, RES, FAST, MK>, g, L, s, p);
       case 2: return launch_with_lds(fmms_dot_kernel<2, EPI, RES, FAST, MK>, g, L, s, p);
@@ -1563,6 +1693,7 @@ static hipError_t launch_masking(const StreamParams& p, const StreamConfig& c, h
     if constexpr (!MK && EPI == EPI_FLAT) return launch_with_lds(fmms_kwide_kernel<EPI>, p.n_tiles, c.lds_bytes, s, p);
     return hipErrorInvalidValue;
   }
+  constexpr bool kNoiseEpi = EPI == EPI_FLAT || EPI == EPI_GROUP;  // epilogues that may read a noise table
   if (c.rm > 0 && !c.dot) {
     switch (c.nb) {
       case 1: return launch_kouter<EPI, MK, 1>(p, c, s);
@@ -1572,9 +1703,9 @@ static hipError_t launch_masking(const StreamParams& p, const StreamConfig& c, h
     }
   }
   if (c.fast) {
-    if (EPI != EPI_STORE && p.noise_pitch > 0 && !c.dot)
-      return res ? launch_variant<EPI, true, true, MK, EPI != EPI_STORE>(p, c, s)
-                 : launch_variant<EPI, false, true, MK, EPI != EPI_STORE>(p, c, s);
+    if (kNoiseEpi && p.noise_pitch > 0 && !c.dot)
+      return res ? launch_variant<EPI, true, true, MK, kNoiseEpi>(p, c, s)
+                 : launch_variant<EPI, false, true, MK, kNoiseEpi>(p, c, s);
     return res ? launch_variant<EPI, true, true, MK, false>(p, c, s) : launch_variant<EPI, false, true, MK, false>(p, c, s);
   }
   return res ? launch_variant<EPI, true, false, MK, false>(p, c, s) : launch_variant<EPI, false, false, MK, false>(p, c, s);

@@ -69,14 +69,28 @@ def kth_score(s_all, k):
     return float(fin[k - 1]) if fin.size >= k else -np.inf
 
 
-def check_ids_topk(gpu_ids, ora_ids, L_rows, rows, T, seed, step0, top_k, mask=None, label=""):
-    """check_ids for top-k sampling, with the top-k boundary reading of the near-tie rule.
+def nucleus_shares(s_all, top_k):
+    """{id: share of the kept mass held by the ids ahead of it} over the top-k ids of a row
+    (scores descending, lower id first), in fp64."""
+    fin = np.flatnonzero(np.isfinite(s_all))
+    order = fin[np.lexsort((fin, -s_all[fin]))][:top_k]
+    if order.size == 0:
+        return {}
+    w = np.exp(s_all[order] - s_all[order[0]])
+    before = np.concatenate([[0.0], np.cumsum(w)[:-1]]) / w.sum()
+    return dict(zip(order.tolist(), before.tolist()))
+
+
+def check_ids_topk(gpu_ids, ora_ids, L_rows, rows, T, seed, step0, top_k, mask=None, label="", top_p=1.0):
+    """check_ids for top-k (and top-p) sampling, with the boundary readings of the near-tie rule.
 
     gpu_ids, ora_ids: [S, R]; L_rows[r] are the oracle's logits of global row rows[r].  A
     mismatch is accepted if it is a near tie of the final argmax among the oracle's kept ids,
     or if the kept sets may differ at the k-th boundary: the GPU's id or the oracle's has a
-    score within 1e-3 (1 + |s_k|) of the k-th largest score s_k.  The GPU's id must always be
-    an allowed id whose score reaches s_k up to that tolerance.  Returns the mismatch count.
+    score within 1e-3 (1 + |s_k|) of the k-th largest score s_k, or, with top_p < 1, at the
+    nucleus boundary: the share of the kept mass ahead of the GPU's id or the oracle's is
+    within 1e-3 of top_p.  The GPU's id must always be an allowed id whose score reaches s_k
+    and whose share ahead stays below top_p, up to those tolerances.  Returns the count.
     """
     gpu_ids = np.asarray(gpu_ids)
     ora_ids = np.asarray(ora_ids)
@@ -91,9 +105,16 @@ def check_ids_topk(gpu_ids, ora_ids, L_rows, rows, T, seed, step0, top_k, mask=N
         sk = kth_score(s_all, top_k)
         tol_k = NEAR_TIE_REL * (1 + abs(sk)) if np.isfinite(sk) else 0.0
         assert s_all[ig] >= sk - tol_k, f"{label}: GPU id {ig} (s={s_all[ig]}) below the k-th score {sk}"
-        p = oracle.perturbed_row(L_rows[r], T, seed, step0 + int(s), int(rows[r]), mask_row=mrow, top_k=top_k)
+        p = oracle.perturbed_row(L_rows[r], T, seed, step0 + int(s), int(rows[r]), mask_row=mrow, top_k=top_k,
+                                 top_p=top_p)
         final_tie = np.isfinite(p[ig]) and float(p[io]) - float(p[ig]) < NEAR_TIE_REL * (1 + abs(float(p[io])))
         boundary = abs(s_all[ig] - sk) < tol_k or abs(s_all[io] - sk) < tol_k
+        if top_p < 1.0:
+            sh = nucleus_shares(s_all, top_k)
+            last = max(sh.values())
+            share_g, share_o = sh.get(ig, last), sh.get(io, last)
+            assert share_g < top_p + NEAR_TIE_REL, f"{label}: GPU id {ig} outside the nucleus (share {share_g})"
+            boundary = boundary or abs(share_g - top_p) < NEAR_TIE_REL or abs(share_o - top_p) < NEAR_TIE_REL
         assert final_tie or boundary, \
             f"{label}: step {s} row {r}: GPU {ig} vs oracle {io} (s {s_all[ig]} / {s_all[io]}, s_k {sk})"
     frac = 1.0 - len(mism) / gpu_ids.size
