@@ -593,6 +593,30 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   return x;
 }
 
+// k-th largest (1-based) of one 32-bit value per lane over the lanes where
+// `valid`, by a most-significant-bit-first select with ballots (no shuffles);
+// on return *rest is that value's rank among the equal values (1-based).
+// 0 if fewer than kth lanes are valid.
+__device__ __forceinline__ uint32_t wave_kth_largest_u32(uint32_t v, bool valid, int kth, int* rest) {
+  if (__popcll(__ballot(valid)) < kth) {
+    *rest = 0;
+    return 0u;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int need = kth;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t m = 1u << bit;
+    const int c = __popcll(__ballot(valid && (v & pmask) == prefix && (v & m) != 0));
+    if (c >= need)
+      prefix |= m;
+    else
+      need -= c;
+    pmask |= m;
+  }
+  *rest = need;
+  return prefix;
+}
+
 struct TopkMergeShared {
   alignas(16) uint64_t F[kTopkMergeCap];  // gathered keys
   uint16_t Ft[kTopkMergeCap];  // tile of each gathered key
@@ -742,11 +766,11 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
     for (int j = 0; j < kTopkLane; ++j) e[w][j] = has ? cand[(int64_t)(w * kTopkSlot + j) * nt + tid] : 0ull;
     hb[w] = has ? cand[(int64_t)(w * kTopkSlot + kTopkLane) * nt + tid] : 0ull;
   }
-  // 1. theta, a lower bound of the row's k-th key: each wave sorts its 64
-  // tile maxima, and the smallest of the four waves' ceil(k/4)-th largest has at
-  // least k keys at or above it.  If a wave holds fewer keys than that, or the
-  // bound gathers more than 32 k entries, theta is the k-th largest tile
-  // maximum itself (ranks by counting over LDS).
+  // 1. theta, a lower bound of the row's k-th key: in each wave the
+  // ceil(k/4)-th largest score among its 64 tile maxima; at least k keys reach
+  // the smallest of the four, so every key with at least that score is gathered.
+  // If a wave holds fewer keys, or the bound gathers more than 32 k entries,
+  // theta is the k-th largest tile maximum itself (ranks by counting over LDS).
   uint64_t x = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) x = e[w][0] > x ? e[w][0] : x;
@@ -754,67 +778,69 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
   sh.rescored[tid] = 0;
   if (tid == 0) {
     sh.theta = 0;
+    sh.tau = 0;
     sh.nF = 0;
     sh.nnew = 0;
   }
   {
-    const uint64_t xs = wave_sort_desc(x);
+    int rest = 0;
     const int kw = (k + kTopkMergeThreads / 64 - 1) / (kTopkMergeThreads / 64);
-    if (lane == kw - 1) sh.Tw[wave] = xs;
+    const uint32_t t = wave_kth_largest_u32((uint32_t)(x >> 32), x != 0, kw, &rest);
+    if (lane == 0) sh.Tw[wave] = t;
   }
   __syncthreads();
-  uint64_t th = ~0ull;
+  uint32_t t32 = 0xFFFFFFFFu;
 #pragma unroll
-  for (int w = 0; w < kTopkMergeThreads / 64; ++w) th = sh.Tw[w] < th ? sh.Tw[w] : th;
+  for (int w = 0; w < kTopkMergeThreads / 64; ++w) t32 = (uint32_t)sh.Tw[w] < t32 ? (uint32_t)sh.Tw[w] : t32;
+  uint64_t th = (uint64_t)t32 << 32, theta = th;
   int cnt = 0;
-  if (th != 0) {
+  if (t32 != 0) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
       for (int j = 0; j < kTopkLane; ++j) cnt += e[w][j] >= th ? 1 : 0;
-    atomicAdd(&sh.nF, cnt);
+    int at = cnt > 0 ? atomicAdd(&sh.nF, cnt) : 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j)
+        if (e[w][j] >= th) {
+          if (at < kTopkMergeCap) {
+            sh.F[at] = e[w][j];
+            sh.Ft[at] = (uint16_t)tid;
+          }
+          ++at;
+        }
   }
   __syncthreads();
-  uint64_t theta = th;
-  if (th == 0 || sh.nF > 32 * k) {
+  if (t32 == 0 || sh.nF > 32 * k) {
     if (x != 0 && rank_in(sh.S, nt, x) == k - 1) sh.theta = x;
     __syncthreads();
     theta = sh.theta;
     th = theta != 0 ? theta : 1ull;  // fewer than k tiles hold a key: gather them all
+    if (tid == 0) sh.nF = 0;
+    __syncthreads();
     cnt = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
       for (int j = 0; j < kTopkLane; ++j) cnt += e[w][j] >= th ? 1 : 0;
+    int at = cnt > 0 ? atomicAdd(&sh.nF, cnt) : 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j)
+        if (e[w][j] >= th) {
+          sh.F[at] = e[w][j];
+          sh.Ft[at] = (uint16_t)tid;
+          ++at;
+        }
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid == 0) sh.nF = 0;
-  __syncthreads();
-  int at = cnt > 0 ? atomicAdd(&sh.nF, cnt) : 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-    for (int j = 0; j < kTopkLane; ++j)
-      if (e[w][j] >= th) {
-        sh.F[at] = e[w][j];
-        sh.Ft[at] = (uint16_t)tid;
-        ++at;
-      }
-  __syncthreads();
-  // 2. tau: the k-th largest gathered key (0 if fewer than k); each gathered key
-  // knows its rank, so the kept ones (rank < k) are known too
+  // 2. tau: the k-th largest gathered key (0 if fewer than k), by ranks
   const int n0 = sh.nF;
-  if (tid == 0) sh.tau = 0;
-  __syncthreads();
-  const uint64_t mykey = tid < n0 ? sh.F[tid] : 0ull;  // one gathered key per thread (n0 <= 32 k)
-  int myrank = INT32_MAX;
-  if (n0 <= kTopkMergeThreads) {
-    if (mykey != 0) myrank = rank_in(sh.F, n0, mykey);
-    if (myrank == k - 1) sh.tau = mykey;
-  } else {
-    for (int i = tid; i < n0; i += kTopkMergeThreads)
-      if (rank_in(sh.F, n0, sh.F[i]) == k - 1) sh.tau = sh.F[i];
-  }
+  for (int i = tid; i < n0; i += kTopkMergeThreads)
+    if (rank_in(sh.F, n0, sh.F[i]) == k - 1) sh.tau = sh.F[i];
   // 3. a tile whose dropped keys could reach tau is rescored
   __syncthreads();
   uint64_t tau = sh.tau;
@@ -827,7 +853,6 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
     atomicAdd(&sh.nnew, 1);
   }
   __syncthreads();
-  bool fast = sh.nnew == 0 && n0 <= kTopkMergeThreads;
   if (sh.nnew != 0) {
     // rebuild: the lists of the other tiles, every id of the rescored ones;
     // repeated while the new tau brings more tiles in
@@ -890,13 +915,9 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
   if (p.top_p < 1.0f) {
     // the kept keys (at most k <= 64) in order into S, then wave 0 cuts them
     __syncthreads();
-    if (fast) {
-      if (myrank < k) sh.S[myrank] = mykey;
-    } else {
-      for (int i = tid; i < n; i += kTopkMergeThreads) {
-        const uint64_t key = sh.F[i];
-        if (key != 0 && key >= tau) sh.S[rank_in(sh.F, n, key)] = key;
-      }
+    for (int i = tid; i < n; i += kTopkMergeThreads) {
+      const uint64_t key = sh.F[i];
+      if (key != 0 && key >= tau) sh.S[rank_in(sh.F, n, key)] = key;
     }
     __syncthreads();
     if (wave == 0) {
@@ -915,11 +936,6 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
         bi = topk_key_id(key);
         bv = topk_key_score(key) + noise_of(bi);
       }
-    }
-  } else if (fast) {
-    if (myrank < k) {
-      bi = topk_key_id(mykey);
-      bv = topk_key_score(mykey) + noise_of(bi);
     }
   } else {
     for (int i = tid; i < n; i += kTopkMergeThreads) {
