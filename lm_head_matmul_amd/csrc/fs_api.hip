@@ -97,7 +97,8 @@ int pow2_at_least(int x) {
   return p;
 }
 
-// Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB, or <= kWideMaxB for the wide kernel).
+// Kernel choice for a batch chunk of `B` rows (B <= kMfmaMaxB, or <= kWideMaxB for the wide kernel,
+// whose chunks run_stream_chunks forms only where that kernel applies).
 int choose_config(int B, int path, fsk::StreamConfig& cfg) {
   // AUTO takes the MFMA kernel at every batch size: on gfx950 it streams W
   // faster than the dot-product kernel even at B = 1 (measured).
@@ -113,7 +114,7 @@ int choose_config(int B, int path, fsk::StreamConfig& cfg) {
   }
   cfg.dot = dot;
   cfg.bd = dot ? pow2_at_least(B) : 0;
-  cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : B <= fsk::kMfmaMaxB ? 4 : 8);
+  cfg.nb = dot ? 0 : (B <= 16 ? 1 : B <= 32 ? 2 : B <= fsk::kMfmaMaxB ? 4 : fsk::wide_nb(B));
   cfg.fast = false;
   cfg.rm = 0;
   cfg.lds_bytes = 0;
@@ -192,9 +193,11 @@ int run_stream_chunks(fs_ctx* ctx, fsk::StreamParams base, int path, int epi, hi
   ctx->prof_before = ctx->prof_after = nullptr;
   int chunk = fsk::kMfmaMaxB < max_rows ? fsk::kMfmaMaxB : max_rows;
   // more than kMfmaMaxB rows of the plain sampler: chunks of kWideMaxB rows for
-  // the wide kernel, which streams W once per chunk
+  // the wide kernel, which streams W once per chunk (any chunk of 65 .. 256
+  // rows, the last one included, needs d to be a multiple of both its k rings)
   if (wide && B > fsk::kMfmaMaxB && max_rows >= fsk::kWideMaxB && path != FS_PATH_DOT && !base.mask &&
-      base.samples <= 1 && base.d % 256 == 0 && epi == fsk::EPI_FLAT)
+      base.samples <= 1 && base.d % fsk::wide_kmult(8) == 0 && base.d % fsk::wide_kmult(16) == 0 &&
+      epi == fsk::EPI_FLAT)
     chunk = fsk::kWideMaxB;
   if (base.mask) {
     const int64_t rows = fsk::kMaskLdsMax / (4 * fsk::tile_mask_words(base.n_mblocks, base.n_tiles));

@@ -36,8 +36,11 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t k0, uint32_t k1, uint3
                                                  uint32_t c3) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t hi_a = __umulhi(0xD2511F53u, c0), lo_a = 0xD2511F53u * c0;
-    const uint32_t hi_b = __umulhi(0xCD9E8D57u, c2), lo_b = 0xCD9E8D57u * c2;
+    // one 32 x 32 -> 64-bit multiply each (a single v_mad_u64_u32) rather than
+    // separate high and low products
+    const uint64_t pa = (uint64_t)0xD2511F53u * c0, pb = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi_a = (uint32_t)(pa >> 32), lo_a = (uint32_t)pa;
+    const uint32_t hi_b = (uint32_t)(pb >> 32), lo_b = (uint32_t)pb;
     const uint32_t n0 = hi_b ^ c1 ^ k0;
     const uint32_t n2 = hi_a ^ c3 ^ k1;
     c1 = lo_b;

@@ -137,7 +137,7 @@ struct CdfParams {
 // Kernel selection for a streaming launch.
 struct StreamConfig {
   bool dot;     // dot-product kernel (else MFMA)
-  int nb;       // MFMA: 16-wide batch blocks (1, 2, 4)
+  int nb;       // MFMA: 16-wide batch blocks (1, 2, 4; 8 or 16: the wide kernel)
   int bd;       // dot: padded batch (1, 2)
   bool fast;    // straight-line fast driver (see fs_stream.h)
   int rm;       // chunked H with the fast driver: rounds per chunk-outer pass (0: round-major kernel)
@@ -152,8 +152,27 @@ constexpr int kDotMaxB = 2;
 constexpr int kFastRingResident = 2;  // register ring depth of the fast driver, H resident (measured best)
 constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exactly this many sub-blocks)
 constexpr int kMfmaMaxB = 64;
-constexpr int kWideMaxB = 128;      // batch chunk of the wide chunk-outer kernel (plain sampler, no mask)
-constexpr int kWideRowBytes = 528;  // its H rows: one 256-wide sub-block + 16 bytes against LDS bank conflicts
+// The wide kernel (65 .. kWideMaxB batch rows of the plain sampler, no mask):
+// kWideWaves waves, each holding wide_mw(NB) x NB accumulator blocks (NB = 8
+// up to 128 rows, 16 above); passes of up to kWideWaves * wide_mw(NB) vocab
+// blocks; H in k-chunks of 32 wide_ksteps(NB), kWideHBufs LDS buffers of
+// wide_bufbytes(NB); W register items of one chunk, wide_ring(NB) of them,
+// each item's loads issued wide_lead(NB) chunks ahead (d must be a multiple
+// of wide_kmult(NB)).
+constexpr int kWideMaxB = 256;
+constexpr int kWideWaves = 4;
+constexpr int kWideHBufs = 3;
+constexpr int wide_nb(int B) { return B <= 128 ? 8 : 16; }
+constexpr int wide_mw(int nb) { return nb == 16 ? 4 : 5; }
+constexpr int wide_ksteps(int nb) { return 2; }
+constexpr int wide_pieces(int nb) { return wide_ksteps(nb) * 4 + 1; }
+constexpr int wide_bufbytes(int nb) { return nb * 16 * wide_pieces(nb) * 16; }
+constexpr int wide_ring(int nb) { return 4; }
+constexpr int wide_lead(int nb) { return 2; }
+constexpr int wide_kmult(int nb) { return 32 * wide_ksteps(nb) * wide_ring(nb); }
+// s_waitcnt immediate that waits until at most n vector-memory loads of the
+// wave are outstanding (expcnt and lgkmcnt left alone)
+constexpr unsigned vmcnt_wait(int n) { return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14) | 0x70u | 0xF00u; }
 // Which 16 bytes of a row's 512-byte sub-block lane group g (0..3) loads with
 // its load instruction e (0..7), and so which 8-value k chunk it feeds to MFMA
 // step e (H is read with the same map): lane_base(g) + e * lane_step bytes.

@@ -1253,24 +1253,24 @@ __global__ void debug_gumbel_scan_init(unsigned long long* stats) {
 // else k-chunks (double-buffered when two fit); the tile's mask words are
 // staged when they fit beside H.  Prefers the layouts the fast driver takes.
 bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
-  if (!cfg.dot && cfg.nb == 8) {
-    // the wide chunk-outer kernel: fixed layout; the plain sampling epilogue,
-    // no mask, one sample per row, whole 256-wide sub-blocks
-    if (epi != EPI_FLAT || p.mask || p.samples > 1 || p.d % 256 != 0 || p.B > kWideMaxB) return false;
-    p.h_rows = kWideMaxB + 1;
-    p.h_rowstride = kWideRowBytes;
+  if (!cfg.dot && cfg.nb > 4) {
+    // the wide kernel: its own H layout; the plain sampling epilogue, no mask,
+    // one sample per row, d a multiple of its k-chunk ring
+    if (epi != EPI_FLAT || p.mask || p.samples > 1 || p.d % wide_kmult(cfg.nb) != 0 || p.B > 16 * cfg.nb) return false;
+    p.h_rows = p.B;
+    p.h_rowstride = wide_pieces(cfg.nb) * 16;
     p.nsub = p.d / 256;
     p.cs = 1;
-    p.nchunk = p.nsub;
-    p.nbuf = 2;
+    p.nchunk = p.d / (32 * wide_ksteps(cfg.nb));
+    p.nbuf = kWideHBufs;
     p.mask_words = 0;
     p.mask_lds_off = 0;
     p.noise_pitch = 0;
     p.noise_lds_off = 0;
     cfg.fast = true;
-    cfg.rm = 2;
+    cfg.rm = 0;
     p.tile_ratio = 0;
-    cfg.lds_bytes = 2 * (kWideMaxB + 1) * kWideRowBytes;  // also covers the final reduction's scratch
+    cfg.lds_bytes = kWideHBufs * wide_bufbytes(cfg.nb);  // also covers the final reduction's scratch
     return cfg.lds_bytes <= kLdsMax;
   }
   if (epi == EPI_TOPK && (cfg.dot || p.n_tiles > kTopkMergeThreads)) return false;  // MFMA kernels only

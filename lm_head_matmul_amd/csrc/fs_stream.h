@@ -106,14 +106,14 @@ __global__ void __launch_bounds__(kThreads)
 
 // Per-wave results (already reduced inside the wave) sit in LDS scratch as
 // [kWaves][Bp] (val, idx, m, s); reduce over waves and publish the tile's entry.
-template <int EPI>
+template <int EPI, int WAVES = kWaves>
 __device__ void publish_tile(const StreamParams& p, const int Bp, const float* sv, const int32_t* si, const float* sm,
                              const float* ss) {
   const int tile = blockIdx.x;
-  for (int b = threadIdx.x; b < p.B; b += kThreads) {
+  for (int b = threadIdx.x; b < p.B; b += WAVES * 64) {
     float v = -INFINITY, m = -INFINITY, s = 0.0f;
     int32_t i = -1;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
       merge_best(v, i, sv[w * Bp + b], si[w * Bp + b]);
       if (EPI == EPI_GROUP) lse_merge(m, s, sm[w * Bp + b], ss[w * Bp + b]);
     }
@@ -263,6 +263,12 @@ __device__ __forceinline__ void h_commit(const u32x4_t (&hs)[kMaxStagePieces], c
 __device__ __forceinline__ void lds_copy16(const void* src, unsigned char* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+// The same copy from a wave-uniform base plus a 32-bit lane byte offset.
+__device__ __forceinline__ void lds_copy16_s(const void* base, uint32_t off, unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -842,7 +848,7 @@ __device__ __forceinline__ void stream_driver(const StreamParams& p, const TileR
 // End of an MFMA streaming kernel: reduce each wave's maximizers over its four
 // lane groups (lanes l16, l16 + 16, l16 + 32, l16 + 48 share a batch column),
 // then over the waves through LDS, and publish the tile's entry.
-template <int EPI, int NB>
+template <int EPI, int NB, int WAVES = kWaves>
 __device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned char* smem, float (&bv)[NB],
                                                  int32_t (&bi)[NB], float (&lm)[NB], float (&ls)[NB]) {
   constexpr int Bp = NB * 16;
@@ -864,21 +870,23 @@ __device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned
   }
   __syncthreads();  // H buffers are free: reuse LDS as scratch
   float* sv = (float*)smem;
-  int32_t* si = (int32_t*)(sv + kWaves * Bp);
-  float* sm = (float*)(si + kWaves * Bp);
-  float* ss = sm + kWaves * Bp;
+  int32_t* si = (int32_t*)(sv + WAVES * Bp);
+  float* sm = (float*)(si + WAVES * Bp);
+  float* ss = sm + WAVES * Bp;
   if (grp == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int b = nb * 16 + l16;
       sv[wave * Bp + b] = bv[nb];
       si[wave * Bp + b] = bi[nb];
-      sm[wave * Bp + b] = lm[nb];
-      ss[wave * Bp + b] = ls[nb];
+      if (EPI == EPI_GROUP) {
+        sm[wave * Bp + b] = lm[nb];
+        ss[wave * Bp + b] = ls[nb];
+      }
     }
   }
   __syncthreads();
-  publish_tile<EPI>(p, Bp, sv, si, sm, ss);
+  publish_tile<EPI, WAVES>(p, Bp, sv, si, sm, ss);
 }
 
 // ---------------------------------------------------------------------------
@@ -1292,194 +1300,324 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
 }
 
 // ---------------------------------------------------------------------------
-// Wide chunk-outer kernel: 128 batch columns (NB = 8) in one pass over W, for
-// batch chunks of 65 .. 128 rows of the plain sampler.  It streams W once per
-// 128 rows instead of once per 64.  H comes in chunks of one 256-wide
-// sub-block: rows padded to kWideRowBytes, row kWideMaxB the zero row the
-// padding lanes read, double-buffered (2 x 129 x 528 B = 136 KB of LDS).  A
-// pass covers RM = 2 rounds (2 x 8 accumulator sets per wave).  In each chunk,
-// round r's item is consumed from register buffer r after the item that
-// follows it -- round 1's, or the next chunk's round 0 -- has been sent to the
-// other buffer.  The chunk order is rotated per workgroup, as in the
-// chunk-outer kernel.
+// Wide kernel: 65 .. 256 batch rows of the plain sampler in one pass over W.
+// At these batch sizes each W byte carries 4 to 16 times the MFMA work of a
+// decode step, and operand reuse in registers decides the speed: a wave keeps
+// a 64 x 16 NB block of logits in accumulators (4 vocab blocks of 16 rows
+// against NB batch blocks of 16 columns), so every W fragment feeds NB MFMAs
+// and every H fragment read from LDS feeds four.  At 256 rows and the MFMA
+// peak that is 64 bytes per clock of LDS reads and 16 of W loads per CU.
+// Four waves, one per SIMD (the accumulators take up to 256 registers), run
+// passes of 16 vocab blocks over the tile: a full pass gives each wave four
+// blocks; the tile's last pass spreads what is left over the waves (missing
+// block slots skip their MFMAs).  H comes through LDS in k-chunks of 32 KSTEPS,
+// three buffers, copied straight from global memory; W goes straight into
+// registers, each chunk's item two chunks ahead of its MFMAs.  The chunk order
+// is rotated per workgroup, as in the chunk-outer kernel.
 // ---------------------------------------------------------------------------
-// Sub-block sb of H rows 0 .. B-1 into buf as whole 1 KB runs of 16-byte
-// pieces (an LDS-direct load writes 64 consecutive pieces): piece j of the
-// buffer is piece j mod 33 of row j / 33, piece 32 of a row being its padding
-// (filled with a copy of piece 0).  Rows past B repeat row B - 1; the runs end
-// before the zero row.  Every wave issues the same fixed number of copies.
-__device__ __forceinline__ void h_sub_dma(const StreamParams& p, int sb, unsigned char* buf) {
-  constexpr int kPieces = kWideRowBytes / 16;                          // 33
-  constexpr int kRunsPerWave = ((kPieces * kWideMaxB + 63) / 64 + kWaves - 1) / kWaves;  // 9
+template <int NB>
+struct WideGeom {
+  static constexpr int KSTEPS = wide_ksteps(NB);
+  static constexpr int PIECES = wide_pieces(NB);  // 16-byte pieces per LDS row, the last one padding
+  static constexpr int ROWBYTES = PIECES * 16;
+  static constexpr int BUFBYTES = wide_bufbytes(NB);
+  static constexpr int RUNS_W = (NB * 16 * PIECES / 64 + kWideWaves - 1) / kWideWaves;  // copies per wave
+  static constexpr int MW = wide_mw(NB);                                                  // vocab block slots per wave
+  static constexpr int NW = MW * KSTEPS;                                                  // W loads per item
+  static_assert(NB * 16 * PIECES % 64 == 0, "a buffer is a whole number of 1 KB runs");
+};
+
+// H k-chunk c (k in [32 KSTEPS c, 32 KSTEPS (c + 1))) into buf, all 16 NB
+// rows, as whole 1 KB runs of 16-byte pieces (an LDS-direct load writes 64
+// consecutive pieces): piece j of the buffer is piece j mod PIECES of row
+// j / PIECES, a row's last piece being padding (a copy of its first).  Rows
+// past B repeat row B - 1, so that a lane's H offsets are affine in its batch
+// block.  Every wave issues RUNS_W copies; runs past the last repeat it,
+// writing the same bytes to the same place.
+// This lane's source offset (bytes from chunk 0 of H) of its piece of each of
+// its RUNS_W runs: the same for every chunk.
+template <int NB>
+__device__ __forceinline__ void h_wide_offsets(const StreamParams& p, uint32_t (&hsrc)[WideGeom<NB>::RUNS_W]) {
+  using G = WideGeom<NB>;
+  constexpr int nrun = NB * 16 * G::PIECES / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nrun = (kPieces * p.B + 63) / 64;
 #pragma unroll
-  for (int k = 0; k < kRunsPerWave; ++k) {
-    const int r0 = wave + k * kWaves;
+  for (int k = 0; k < G::RUNS_W; ++k) {
+    const int r0 = wave + k * kWideWaves;
     const int run = r0 < nrun ? r0 : nrun - 1;
     const int piece = run * 64 + lane;
-    const int row = piece / kPieces, col = piece - row * kPieces;
+    const int row = piece / G::PIECES, col = piece - row * G::PIECES;
     const int srow = row < p.B ? row : p.B - 1;
-    const int scol = col < kPieces - 1 ? col : 0;
-    lds_copy16(p.H + (int64_t)srow * p.ldh + sb * 256 + scol * 8, buf + run * 1024);
+    const int scol = col < G::PIECES - 1 ? col : 0;
+    hsrc[k] = (uint32_t)(srow * p.ldh + scol * 8) * 2u;
   }
 }
 
-template <int EPI>
-__global__ void __launch_bounds__(kThreads) fmms_kwide_kernel(const StreamParams p) {
-  constexpr int NB = 8, RM = 2;
-  constexpr int LAYOUT = kLayoutKouter;
-  constexpr int bufbytes = (kWideMaxB + 1) * kWideRowBytes;
-  static_assert(NB * 16 == kWideMaxB, "one batch column per lane group row");
+// Run k of this wave's copies of H chunk c into buf.
+template <int NB>
+__device__ __forceinline__ void h_wide_run(const StreamParams& p, int c, unsigned char* buf,
+                                           const uint32_t (&hsrc)[WideGeom<NB>::RUNS_W], int k) {
+  using G = WideGeom<NB>;
+  constexpr int nrun = NB * 16 * G::PIECES / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = wave + k * kWideWaves;
+  const int run = r0 < nrun ? r0 : nrun - 1;
+  lds_copy16_s((const char*)p.H + c * (64 * G::KSTEPS), hsrc[k], buf + run * 1024);
+}
+
+template <int NB>
+__device__ __forceinline__ void h_wide_dma(const StreamParams& p, int c, unsigned char* buf,
+                                           const uint32_t (&hsrc)[WideGeom<NB>::RUNS_W]) {
+#pragma unroll
+  for (int k = 0; k < WideGeom<NB>::RUNS_W; ++k) h_wide_run<NB>(p, c, buf, hsrc, k);
+}
+
+// The loads of one W item: per block slot, a scalar base (the block's rows
+// at the chunk's k offset) and the lane's offset in it.
+template <int MW>
+struct WideItem {
+  const char* base[MW];
+  uint32_t off[MW];
+};
+
+// The MFMAs of one k-chunk, group by group (a group: one 32-wide k-step
+// against four batch blocks, for the wave's four vocab block slots), with the
+// vector-memory work of a later chunk spread over the groups: the copies of
+// H chunk c3 into hbuf3, then the W item `it` into dst.  Issued in one burst,
+// those loads held the wave up for as long as the CU's address unit took to
+// accept them, with no MFMA in flight; spread out, each slice issues while
+// the matrix core works through the previous group.  Each group's H fragments
+// are read one group ahead.  Block slots past the wave's block count compute
+// on repeated rows and are discarded: a run-time skip would split the
+// accumulators' live ranges over two paths, which the register allocator
+// answered with a copy of all of them per chunk.
+template <int NB, int GI>
+__device__ __forceinline__ void wide_groups(const u32x4_t (&w)[wide_mw(NB)][wide_ksteps(NB)], const unsigned char* hb,
+                                            f32x4_t (&acc)[wide_mw(NB)][NB], u32x4_t (&h)[2][4], const StreamParams& p, int c3,
+                                            unsigned char* hbuf3, const uint32_t (&hsrc)[WideGeom<NB>::RUNS_W],
+                                            const WideItem<wide_mw(NB)>& it,
+                                            u32x4_t (&dst)[wide_mw(NB)][wide_ksteps(NB)]) {
+  constexpr int KS = wide_ksteps(NB), MW = wide_mw(NB), NG = NB / 4, NGRP = KS * NG;
+  constexpr int BLK = 16 * WideGeom<NB>::ROWBYTES;  // LDS bytes between batch blocks
+  constexpr int RUNS = WideGeom<NB>::RUNS_W, PIECES = RUNS + MW * KS;
+  if constexpr (GI < NGRP) {
+    constexpr int j0 = GI * PIECES / NGRP, j1 = (GI + 1) * PIECES / NGRP;
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      if (j < RUNS) {
+        h_wide_run<NB>(p, c3, hbuf3, hsrc, j);
+      } else {
+        const int m = (j - RUNS) / KS, e = (j - RUNS) % KS;
+        dst[m][e] = *(const u32x4_t*)(it.base[m] + it.off[m] + e * 64);
+      }
+    }
+    if constexpr (GI + 1 < NGRP) {
+      constexpr int e1 = (GI + 1) / NG, ng1 = (GI + 1) % NG;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[(GI + 1) & 1][q] = *(const u32x4_t*)(hb + (ng1 * 4 + q) * BLK + e1 * 64);
+    }
+    constexpr int e = GI / NG, ng = GI % NG;
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[m][ng * 4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[m][e]),
+                                                                     __builtin_bit_cast(bf16x8_t, h[GI & 1][q]),
+                                                                     acc[m][ng * 4 + q], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wide_groups<NB, GI + 1>(w, hb, acc, h, p, c3, hbuf3, hsrc, it, dst);
+  }
+}
+
+// Pass q of a tile: the tile's blocks split into npass near-equal passes of
+// at most kWideWaves * MW blocks; wave w's first block and block count in it
+// (the lower waves take one more where the pass does not divide by four; none
+// past the last pass, where the tile's last block stands in for the loads).
+__device__ __forceinline__ void wide_geom(int mb_lo, int mb_hi, int q, int npass, int wave, int& mb0, int& mw) {
+  if (q >= npass) {
+    mb0 = mb_hi - 1;
+    mw = 0;
+    return;
+  }
+  const int nblk = mb_hi - mb_lo;
+  const int lo = mb_lo + q * nblk / npass;
+  const int n = mb_lo + (q + 1) * nblk / npass - lo;
+  const int base = n >> 2, extra = n & 3;
+  mw = base + (wave < extra ? 1 : 0);
+  mb0 = lo + wave * base + (wave < extra ? wave : extra);
+}
+
+// The W item of chunk c of pass q: for block slots m = 0..3, the lane's 16
+// bytes of each of the chunk's k-steps (kouter layout: lane group g feeds k
+// values 8 g .. 8 g + 7 of each 32-wide step).  Slots past the wave's block
+// count repeat its last block (the tile's last with none), so that every item
+// issues the same loads; rows of the tile's last block are clamped to its end
+// (off_delta).
+template <int NB>
+__device__ __forceinline__ WideItem<wide_mw(NB)> wide_item(const StreamParams& p, int mb_lo, int mb_hi, int npass,
+                                                           int wave, uint32_t off_full, uint32_t off_delta, int q,
+                                                           int c) {
+  int mb0, mw;
+  wide_geom(mb_lo, mb_hi, q, npass, wave, mb0, mw);
+  WideItem<wide_mw(NB)> it;
+#pragma unroll
+  for (int m = 0; m < wide_mw(NB); ++m) {
+    const int mb = mw == 0 ? mb_hi - 1 : mb0 + (m < mw ? m : mw - 1);
+    it.base[m] = (const char*)p.W + (int64_t)mb * 16 * p.ldw * 2 + c * (wide_ksteps(NB) * 64);
+    it.off[m] = off_full + (mb == mb_hi - 1 ? off_delta : 0u);
+  }
+  return it;
+}
+
+template <int NB>
+__device__ __forceinline__ void wide_wload(const WideItem<wide_mw(NB)>& it,
+                                           u32x4_t (&dst)[wide_mw(NB)][wide_ksteps(NB)]) {
+#pragma unroll
+  for (int m = 0; m < wide_mw(NB); ++m)
+#pragma unroll
+    for (int e = 0; e < wide_ksteps(NB); ++e) dst[m][e] = *(const u32x4_t*)(it.base[m] + it.off[m] + e * 64);
+}
+
+template <int NB>
+__global__ void __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fmms_wide_kernel(const StreamParams p) {
+  using G = WideGeom<NB>;
+  constexpr int KS = G::KSTEPS, MW = G::MW;
+  constexpr int RING = wide_ring(NB), LEAD = wide_lead(NB);
+  static_assert(LEAD >= 2 && LEAD < RING, "an item's slot is free once its chunk's MFMAs ran");
+  // The wait at the start of item t leaves at most WAIT loads and copies in
+  // flight.  The copies of chunk t + 1 went out in item t - 1, before the W
+  // items of chunks t + LEAD - 1 and, from item t - 1 on, t + LEAD ... what
+  // chunk t needs is everything up to them.  The compiler counts only the W
+  // loads (not the copies), and unless the wait also leaves at most the W
+  // items after chunk t's in flight by its count, it adds a wait of its own
+  // before the MFMAs that drains more; so the wait is the smaller of the two.
+  constexpr int NEED = LEAD == 2 ? G::NW + G::RUNS_W : 2 * G::NW + G::RUNS_W;
+  constexpr int WAIT = NEED < (LEAD - 1) * G::NW ? NEED : (LEAD - 1) * G::NW;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
   const TileRange tr = tile_range(p);
-  int hoff[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = nb * 16 + l16;
-    hoff[nb] = lane_base<LAYOUT>(grp) + (row < p.B ? row : kWideMaxB) * kWideRowBytes;
-  }
-  float bv[NB], lm[NB], ls[NB];
+  // the tile's blocks as wave-uniform 32-bit values (block counts are far below
+  // 2^31), so that the W addressing runs on the scalar unit
+  const int mb_lo = __builtin_amdgcn_readfirstlane((int)tr.mb_lo);
+  const int mb_hi = __builtin_amdgcn_readfirstlane((int)tr.mb_hi);
+  const int nchunk = p.d / (32 * KS);
+  const int npass = (mb_hi - mb_lo + kWideWaves * MW - 1) / (kWideWaves * MW);
+  const int rot = (int)(blockIdx.x % (unsigned)nchunk);
+  // this lane's H fragment in batch block 0 (the others follow at fixed
+  // offsets: rows past B hold copies of row B - 1)
+  const int hoff = (l16 < p.B ? l16 : p.B - 1) * G::ROWBYTES + grp * 16;
+  const WLane wl = w_lane<kLayoutKouter>(p, tr, l16, grp);
+  const uint32_t off_full = wl.full, off_delta = wl.last - wl.full;  // rows of the tile's last block are clamped
+  float bv[NB], lm[NB], ls[NB];  // lm, ls: unused by the plain sampler
   int32_t bi[NB];
+  f32x4_t acc[MW][NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     bv[nb] = -INFINITY;
     bi[nb] = -1;
     lm[nb] = -INFINITY;
     ls[nb] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MW; ++m) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  f32x4_t acc[RM][NB];
-#pragma unroll
-  for (int r = 0; r < RM; ++r)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t wb[RING][MW][KS];
 
-  const int nchunk = p.nsub;  // one sub-block per chunk
-  const int npass = (tr.rounds + RM - 1) / RM;
-  auto blk = [&](int pass, int r) { return tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave; };
-  const WLane wl = w_lane<LAYOUT>(p, tr, l16, grp);
-  auto load = [&](u32x4_t (&buf)[8], int64_t mb, int sb) { w_load8<LAYOUT>(p, tr, wl, mb, sb, buf); };
-  // One item: the 8 k-steps of its sub-block against the 8 batch blocks, in two
-  // halves of 4 blocks (the W registers serve both; B operands for only 4
-  // blocks are held, one k-step ahead).
-  auto compute = [&](const u32x4_t (&cur)[8], const unsigned char* hb, f32x4_t (&a)[NB]) {
+  // chunks 0 and 1's H, then the W items of chunks 0 .. LEAD-1 (all of pass 0:
+  // nchunk is a multiple of RING)
+  uint32_t hsrc[G::RUNS_W];
+  h_wide_offsets<NB>(p, hsrc);
+  h_wide_dma<NB>(p, rot, smem, hsrc);
+  h_wide_dma<NB>(p, rot + 1 < nchunk ? rot + 1 : 0, smem + G::BUFBYTES, hsrc);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4_t h0[4], h1[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) h0[q] = *(const u32x4_t*)(hb + hoff[hf * 4 + q]);
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          h1[q] = *(const u32x4_t*)(hb + hoff[hf * 4 + q] + (j + 1) * lane_step<LAYOUT>());
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          a[hf * 4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
-                                                                  __builtin_bit_cast(bf16x8_t, h0[q]), a[hf * 4 + q],
-                                                                  0, 0, 0);
-        if (j + 2 < 8) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            h0[q] = *(const u32x4_t*)(hb + hoff[hf * 4 + q] + (j + 2) * lane_step<LAYOUT>());
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          a[hf * 4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j + 1]),
-                                                                  __builtin_bit_cast(bf16x8_t, h1[q]), a[hf * 4 + q],
-                                                                  0, 0, 0);
-      }
-    }
-  };
-  auto finish = [&](int pass, int r, f32x4_t (&a)[NB]) {
-    const int64_t mbg = tr.mb_lo + (int64_t)(pass * RM + r) * kWaves + wave;
-    if (mbg < tr.mb_hi) {
-      const int v0 = (int)(mbg * 16) + grp * 4;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int b = nb * 16 + l16;
-        if (b < p.B) {
-          const float a4[4] = {a[nb][0], a[nb][1], a[nb][2], a[nb][3]};
-          const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), b);
-          epilogue_quad<EPI>(p, v0, a4, g, 0xFu, bv[nb], bi[nb], lm[nb], ls[nb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // one N-block's noise at a time (register pressure)
-      }
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) a[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-
-  if (tr.rounds > 0) {
-    for (int i = tid; i < kWideRowBytes / 16; i += kThreads) {  // the zero row of both buffers
-      *(u32x4_t*)(smem + kWideMaxB * kWideRowBytes + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
-      *(u32x4_t*)(smem + bufbytes + kWideMaxB * kWideRowBytes + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
-    }
-    const int rot = (int)(blockIdx.x % (unsigned)nchunk);
-    h_sub_dma(p, rot, smem);
-    u32x4_t buf[2][8];
-    load(buf[0], blk(0, 0), rot);
-    // the first W item is in flight behind the chunk's copies: once at most its
-    // 8 loads remain (vmcnt 8), this wave's copies have landed
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xF78);
-    __syncthreads();
-    int cc = 0;
-    for (int pass = 0; pass < npass; ++pass) {
-      for (int cpos = 0; cpos < nchunk; ++cpos) {
-        const int c = cpos + rot < nchunk ? cpos + rot : cpos + rot - nchunk;
-        const int nc = c + 1 < nchunk ? c + 1 : 0;
-        const bool last_c = cpos + 1 == nchunk;  // the pass's k reduction completes here
-        const unsigned char* hb = smem + (cc & 1) * bufbytes;
-        // the item after this chunk's round 1: the next chunk's round 0, or the next pass's
-        const int64_t next_mb = last_c ? blk(pass + 1 < npass ? pass + 1 : pass, 0) : blk(pass, 0);
-        const int next_sb = last_c ? rot : nc;
-        load(buf[1], blk(pass, 1), c);
-        // the next chunk's H, also after the last one (unused then): a copy on
-        // one path only would leave the compiler unsure of the loads in flight
-        h_sub_dma(p, nc, smem + ((cc + 1) & 1) * bufbytes);
-        __builtin_amdgcn_sched_barrier(0);
-        // waves w and w + 4 share a SIMD: the higher priority alternates between
-        // them round by round (as in the chunk-outer kernel)
-        if ((wave >> 2) != 0)
-          __builtin_amdgcn_s_setprio(1);
-        else
-          __builtin_amdgcn_s_setprio(0);
-        compute(buf[0], hb, acc[0]);
-        if (last_c) {
-          __builtin_amdgcn_sched_barrier(0);
-          finish(pass, 0, acc[0]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        load(buf[0], next_mb, next_sb);
-        __builtin_amdgcn_sched_barrier(0);
-        // a pass's round 1 past the tile's last round (odd round counts) is
-        // skipped by the whole workgroup; its load is left in place (it reads
-        // the tile's last block again) so that every chunk issues the same loads
-        if ((wave >> 2) != 0)
-          __builtin_amdgcn_s_setprio(0);
-        else
-          __builtin_amdgcn_s_setprio(1);
-        if (pass * RM + 1 < tr.rounds) compute(buf[1], hb, acc[1]);
-        if (last_c) {
-          __builtin_amdgcn_sched_barrier(0);
-          finish(pass, 1, acc[1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // the chunk's copies were issued before the last W item (8 loads)
-        __builtin_amdgcn_s_waitcnt(0xF78);
-        __syncthreads();
-        ++cc;
-      }
-    }
+  for (int j = 0; j < LEAD; ++j)
+    wide_wload<NB>(wide_item<NB>(p, mb_lo, mb_hi, npass, wave, off_full, off_delta, 0,
+                                 rot + j < nchunk ? rot + j : rot + j - nchunk),
+                   wb[j]);
+  int hcur = 0;  // LDS buffer of the current chunk (chunk t uses buffer t mod 3)
+  for (int q = 0; q < npass; ++q) {
+    int mb0, mw;
+    wide_geom(mb_lo, mb_hi, q, npass, wave, mb0, mw);
+    for (int cpos = 0; cpos < nchunk; cpos += RING) {
+      // the RING items of the register ring, written out so that every index
+      // into the ring and the accumulators is a constant from the start
+#define FS_WIDE_ITEM(r)                                                                    \
+  if constexpr ((r) < RING) {                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(WAIT));                                          \
+    __syncthreads();                                                                       \
+    const int n2 = cpos + (r) + LEAD;                                                      \
+    const int q2 = n2 >= nchunk ? q + 1 : q;                                               \
+    const int cp2 = n2 >= nchunk ? n2 - nchunk : n2;                                       \
+    const int c2 = cp2 + rot < nchunk ? cp2 + rot : cp2 + rot - nchunk;                    \
+    const int n3 = cpos + (r) + 2;                                                         \
+    const int cp3 = n3 >= nchunk ? n3 - nchunk : n3;                                       \
+    const int c3 = cp3 + rot < nchunk ? cp3 + rot : cp3 + rot - nchunk;                    \
+    const WideItem<MW> it = wide_item<NB>(p, mb_lo, mb_hi, npass, wave, off_full, off_delta, q2, c2); \
+    const unsigned char* hb = smem + hcur * G::BUFBYTES + hoff;                            \
+    u32x4_t h[2][4];                                                                       \
+    _Pragma("unroll") for (int qq = 0; qq < 4; ++qq) h[0][qq] =                             \
+        *(const u32x4_t*)(hb + qq * 16 * G::ROWBYTES);                                     \
+    wide_groups<NB, 0>(wb[(r) % RING], hb, acc, h, p, c3,                                  \
+                       smem + (hcur == 0 ? 2 : hcur - 1) * G::BUFBYTES, hsrc, it,          \
+                       wb[((r) + LEAD) % RING]);                                           \
+    hcur = hcur == 2 ? 0 : hcur + 1;                                                       \
   }
-  finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
+      // Each item t: everything but the last three batches issued (chunk
+      // t + LEAD - 1's W item, chunk t + 2's copies, chunk t + LEAD's W item)
+      // has landed, which covers this wave's copies of chunk t + 1 and its W
+      // item of chunk t + 1 (the W loads are visible to the compiler, the
+      // copies are not, so its own waits only ever cover more); the barrier
+      // makes every wave's copies of chunk t visible and frees buffer
+      // (t + 2) mod 3; chunk t + 2's copies and chunk t + LEAD's W item go out;
+      // chunk t's MFMAs run.
+      static_assert(RING <= 8, "items written out below");
+      FS_WIDE_ITEM(0)
+      FS_WIDE_ITEM(1)
+      FS_WIDE_ITEM(2)
+      FS_WIDE_ITEM(3)
+      FS_WIDE_ITEM(4)
+      FS_WIDE_ITEM(5)
+      FS_WIDE_ITEM(6)
+      FS_WIDE_ITEM(7)
+#undef FS_WIDE_ITEM
+    }
+    // the pass's epilogue, one vocab block slot at a time (written out: see
+    // the items above); the next two chunks' copies and W loads are in flight
+#define FS_WIDE_EPI(m)                                                                            \
+  if constexpr ((m) < MW) {                                                                       \
+    if ((m) < mw) {                                                                               \
+      const int v0 = (int)((mb0 + (m)) * 16) + grp * 4;                                           \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                         \
+        const int b = nb * 16 + l16;                                                              \
+        if (b < p.B) {                                                                            \
+          const float a4[4] = {acc[m][nb][0], acc[m][nb][1], acc[m][nb][2], acc[m][nb][3]};       \
+          const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), b);                         \
+          epilogue_quad<EPI_FLAT>(p, v0, a4, g, 0xFu, bv[nb], bi[nb], lm[nb], ls[nb]);            \
+        }                                                                                         \
+        __builtin_amdgcn_sched_barrier(0); /* one quad's noise at a time (registers) */          \
+      }                                                                                           \
+    }                                                                                             \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};   \
+  }
+    FS_WIDE_EPI(0)
+    FS_WIDE_EPI(1)
+    FS_WIDE_EPI(2)
+    FS_WIDE_EPI(3)
+    FS_WIDE_EPI(4)
+    FS_WIDE_EPI(5)
+    FS_WIDE_EPI(6)
+    FS_WIDE_EPI(7)
+    static_assert(MW <= 8, "block slots written out above");
+#undef FS_WIDE_EPI
+  }
+  // the copies past the last chunk write LDS: all of them land before it is reused
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  finish_wave_tile<EPI_FLAT, NB, kWideWaves>(p, smem, bv, bi, lm, ls);
 }
 
 // ---------------------------------------------------------------------------
@@ -1629,7 +1767,8 @@ __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p
 // The dynamic-LDS limit of each kernel is raised to the full budget once per
 // device (the attribute call is far slower than a launch).
 template <typename K>
-static hipError_t launch_with_lds(K kernel, int grid, int lds, hipStream_t stream, const StreamParams& p) {
+static hipError_t launch_with_lds(K kernel, int grid, int lds, hipStream_t stream, const StreamParams& p,
+                                  int threads = kThreads) {
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1640,7 +1779,7 @@ static hipError_t launch_with_lds(K kernel, int grid, int lds, hipStream_t strea
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -1689,8 +1828,11 @@ static hipError_t launch_kouter(const StreamParams& p, const StreamConfig& c, hi
 template <int EPI, bool MK>
 static hipError_t launch_masking(const StreamParams& p, const StreamConfig& c, hipStream_t s) {
   const bool res = p.nchunk == 1;
-  if (c.nb == 8) {
-    if constexpr (!MK && EPI == EPI_FLAT) return launch_with_lds(fmms_kwide_kernel<EPI>, p.n_tiles, c.lds_bytes, s, p);
+  if (c.nb > 4) {  // the wide kernel
+    if constexpr (!MK && EPI == EPI_FLAT) {
+      if (c.nb == 8) return launch_with_lds(fmms_wide_kernel<8>, p.n_tiles, c.lds_bytes, s, p, kWideWaves * 64);
+      if (c.nb == 16) return launch_with_lds(fmms_wide_kernel<16>, p.n_tiles, c.lds_bytes, s, p, kWideWaves * 64);
+    }
     return hipErrorInvalidValue;
   }
   constexpr bool kNoiseEpi = EPI == EPI_FLAT || EPI == EPI_GROUP;  // epilogues that may read a noise table

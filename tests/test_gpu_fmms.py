@@ -37,7 +37,7 @@ def fs():
 def ctx(fs):
     import torch
 
-    c = fs.fs_create(0, max_B=256, max_V=262144, max_top_k=64)
+    c = fs.fs_create(0, max_B=320, max_V=262144, max_top_k=64)
     torch.cuda.synchronize()
     yield c
     torch.cuda.synchronize()
@@ -185,8 +185,15 @@ RAGGED = [
     (2, 86016, 300, 1.0, 1), (2, 16, 7, 1.0, 0), (16, 20480, 300, 1.0, 2),
     # rows of more than 8 sub-blocks with H resident: the kernel with the tile's noise table
     (5, 3072, 3001, 0.8, 0), (16, 2560, 2049, 1.0, 0), (1, 4096, 5000, 1.0, 0),
-    # the wide kernel's 128-row chunks: two of them and a tail, a chunk of one row after it
-    (200, 512, 3001, 0.9, 0), (129, 256, 1500, 1.0, 0), (128, 2048, 4099, 0.7, 0),
+    # the wide kernel (65 .. 256 rows, d a multiple of 256): eight batch blocks
+    # and sixteen, rows past B in the last block, tiles of one vocab block (the
+    # other waves' slots empty), tiles of more than one pass with a partial
+    # last pass, a batch split into 256 rows and a tail of 44 or 1
+    (65, 512, 999, 1.0, 0), (100, 1024, 777, 0.8, 0), (128, 2048, 4099, 0.7, 0), (129, 512, 1500, 1.0, 0),
+    (200, 512, 3001, 0.9, 0), (256, 1024, 9001, 0.8, 0), (136, 512, 70001, 1.0, 0), (300, 512, 2000, 1.0, 0),
+    (257, 512, 1000, 1.1, 0),
+    # more than 64 rows with d not a multiple of 256: 64-row chunks
+    (129, 264, 1500, 1.0, 0), (70, 520, 999, 1.0, 0),
     # more than 16 rows at d <= 2048: H in chunks although it would fit in LDS
     (24, 2048, 3001, 0.9, 0), (32, 1024, 2000, 1.0, 0),
 ]
@@ -469,9 +476,10 @@ def test_group_summaries_match_group_by_group_calls(fs, ctx):
     assert diff.mean() <= 1e-3 + 1e-9 or np.all(np.abs(a[1][diff] - b[1][diff]) < 1e-3 * (1 + np.abs(b[1][diff])))
 
 
-@pytest.mark.parametrize("B,d,V", [(100, 512, 3001), (128, 1024, 5000)])
+@pytest.mark.parametrize("B,d,V", [(100, 512, 3001), (128, 1024, 5000), (200, 512, 3001), (256, 512, 70001)])
 def test_tile_maxima_wide(fs, ctx, B, d, V):
-    # per-tile maximizers of the wide kernel (128-row chunks) against the oracle's
+    # per-tile maximizers of the wide kernel (eight and sixteen batch blocks,
+    # tiles of one pass and of several) against the oracle's
     import torch
 
     H = synth.normal_bf16(B, d, seed=300 + B)
