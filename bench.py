@@ -109,12 +109,13 @@ def measured_traffic(op="fused", workload="mid_decode", B=64):
 
 def profile_cmds(op, workload, B):
     a = f"--profile --profile-op {op} --workload {workload} --batch {B}"
+    d = f"gpurun_out/prof_{op}_{workload}_B{B}"
     return {
-        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{op}_trace -o trace "
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}_trace -o trace "
                  f"-- python3 bench.py {a} --steps 1000 --warmup 50",
-        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_{op}_fetch -o fetch "
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}_fetch -o fetch "
                  f"-- python3 bench.py {a} --steps 5 --warmup 2",
-        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_{op}_write -o write "
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}_write -o write "
                  f"-- python3 bench.py {a} --steps 5 --warmup 2",
     }
 

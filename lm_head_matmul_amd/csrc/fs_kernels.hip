@@ -561,9 +561,13 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams
 // on the keys that wave dropped.  [readus.org FlashSampling summary, section on
 // Top-K and masking: a pre-filter keeps candidates, exact Gumbel-Max runs on
 // them]  Keys order (score desc, id asc); the row's top-k is the k largest.
-//   1. theta = the k-th largest tile maximum.  k distinct ids reach it, so the
-//      row's k-th key tau is at least theta, and only list entries >= theta can
-//      be kept: they are gathered (at most 32 k of them).
+//   1. theta, a lower bound of the row's k-th key tau: each wave takes the
+//      ceil(k/4)-th largest score word of its 64 tiles' maxima (a ballot
+//      select); the smallest of the four leaves at least k tile maxima, i.e. k
+//      distinct ids, at or above it.  Only list entries >= theta can be kept:
+//      they are gathered.  Without such a bound, or if it gathers more than
+//      32 k entries, theta is the k-th largest tile maximum itself (then at
+//      most 32 k entries reach it).
 //   2. tau = the k-th largest gathered key (0 = keep all if there are fewer).
 //   3. A wave whose bound reaches tau may have dropped a kept id.  Then its
 //      tile is rescored (every id of the tile recomputed from H and W in fp32)
