@@ -89,7 +89,8 @@ const char* fs_last_error(void);
  * NULL, receives n_tiles + 1 ascending vocab ids: tile i covers
  * [bounds[i], bounds[i+1]).  Tiles are contiguous and balanced in units of 16
  * vocab rows.  Calls that do not report tile maxima may size the tiles per
- * XCD instead (the sampled ids do not depend on the tiling). */
+ * XCD instead (the tiling changes only the order of the fp32 sums behind the
+ * logits, so the sampled ids agree except at near ties). */
 int fs_fmms_tiling(fs_ctx* ctx, int B, int d, int64_t V, int path, int64_t* n_tiles, int64_t* bounds);
 
 /* Fused LM-head matmul + sample (FMMS).
