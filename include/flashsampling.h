@@ -219,6 +219,31 @@ int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh
                        int B, int d, int64_t vocab_offset, int64_t G, int n_groups, float temperature, uint64_t seed,
                        uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out, int path);
 
+/* Online grouped producer: fs_group_summaries whose groups are consumed as
+ * they are published.  The tiles of group k (the launch gives each group an
+ * equal share of the GPU's workgroups) start streaming only once ready[k]
+ * equals epoch, so a producer -- the host writing a flag in pinned host
+ * memory, or work on another stream -- can hand over group k's rows of W while
+ * the launch already runs on the groups before it; with every flag already set
+ * it is fs_group_summaries.
+ *   ready [n_groups] uint32, device memory or pinned host memory mapped into
+ *     the device (read with system-scope acquire loads); the producer writes
+ *     epoch to ready[k] after group k's rows of W are in place (a release).
+ *   max_wait_us: bound of each tile's wait (at most 60 s).  A tile whose flag
+ *     does not arrive in time does no work and sets *status (device int32,
+ *     caller-owned, not cleared by this call) to 1; that group's summaries
+ *     are then unspecified.
+ *   Everything else as in fs_group_summaries.
+ *   [arXiv 2603.15854 abstract: grouped variants for online settings;
+ *    readus.org summary, "Group Gumbel Max"]
+ * Errors as fs_group_summaries; also FS_ERR_INVALID_ARG for a NULL ready or
+ * status. */
+int fs_group_summaries_online(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W,
+                              int64_t ldw, int B, int d, int64_t vocab_offset, int64_t G, int n_groups,
+                              float temperature, uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm,
+                              const uint32_t* ready, uint32_t epoch, uint32_t max_wait_us, int32_t* status,
+                              fs_group_summary_t* out, int path);
+
 /* Combine per-group summaries s [n_groups, B] (group-major) into one sample
  * per row.
  *   FS_COMBINE_GUMBEL: k* = argmax_k (lse_k + g'_k) with g'_k the Gumbel

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     fs_fmms_tiling,
     fs_group_combine,
     fs_group_summaries,
+    fs_group_summaries_online,
     fs_group_summary,
     fs_last_error,
     fs_profile_next_launch,

@@ -49,6 +49,8 @@ SIGNATURES = {
     "fs_group_summary": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _F, _U64, _U64, _P, _I64, _P, _I]),
     "fs_group_summaries": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _I, _F, _U64, _U64, _P, _I64, _P,
                                 _I]),
+    "fs_group_summaries_online": (_I, [_P, _P, _P, _I64, _P, _I64, _I, _I, _I64, _I64, _I, _F, _U64, _U64, _P, _I64,
+                                       _P, ctypes.c_uint32, ctypes.c_uint32, _P, _P, _I]),
     "fs_group_combine": (_I, [_P, _P, _P, _I, _I, _U64, _U64, _I, _P]),
     "fs_fmms_sample_noalloc": (_I, [_P, _P, _I64, _P, _I64, _I, _I, _I64, _F, _U64, _U64, _P, _I64, _P]),
     "fs_profile_next_launch": (_I, [_P, _P, _P]),
@@ -322,6 +324,36 @@ def fs_group_summaries(ctx: int, H: torch.Tensor, W: torch.Tensor, vocab_offset:
     _check(_lib.fs_group_summaries(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d, vocab_offset,
                                    group_size, n_groups, float(temperature), seed, step, mptr, ldm, out.data_ptr(),
                                    path))
+    return out
+
+
+def fs_group_summaries_online(ctx: int, H: torch.Tensor, W: torch.Tensor, vocab_offset: int, group_size: int,
+                              temperature: float, seed: int, step: int, ready: torch.Tensor, epoch: int,
+                              status: torch.Tensor, max_wait_us: int = 1_000_000, mask: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None, path: int = FS_PATH_AUTO,
+                              stream=None) -> torch.Tensor:
+    """fs_group_summaries whose group k starts once ready[k] == epoch.  ready: [n_groups] int32 on the GPU or in
+    pinned host memory; status: one int32 on the GPU, set to 1 if a group's wait ran out."""
+    B, d, ldh = _matrix(H, "H")
+    V, d2, ldw = _matrix(W, "W")
+    if d2 != d:
+        raise ValueError("H and W disagree on d")
+    if group_size < 1 or V % group_size != 0:
+        raise ValueError("W's rows must be a whole number of groups")
+    n_groups = V // group_size
+    if ready.dtype != torch.int32 or not ready.is_contiguous() or ready.numel() < n_groups:
+        raise TypeError(f"ready must be a contiguous int32 tensor of at least {n_groups} flags")
+    if not (ready.is_cuda or ready.is_pinned()):
+        raise ValueError("ready must live on the GPU or in pinned host memory")
+    _device_buffer(status, torch.int32, 1, "status")
+    if out is None:
+        out = torch.empty((n_groups, B, 3), dtype=torch.int32, device=H.device)
+    _device_buffer(out, torch.int32, n_groups * B * 3, "out")
+    mptr, ldm = _mask_args(mask, B, vocab_offset + V)
+    _check(_lib.fs_group_summaries_online(ctx, _stream_ptr(stream), H.data_ptr(), ldh, W.data_ptr(), ldw, B, d,
+                                          vocab_offset, group_size, n_groups, float(temperature), seed, step, mptr, ldm,
+                                          ready.data_ptr(), epoch & 0xFFFFFFFF, max_wait_us, status.data_ptr(),
+                                          out.data_ptr(), path))
     return out
 
 

@@ -697,9 +697,13 @@ int fs_group_summary(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, 
   });
 }
 
-int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
-                       int B, int d, int64_t vocab_offset, int64_t G, int n_groups, float temperature, uint64_t seed,
-                       uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out, int path) {
+// Summaries of n_groups consecutive groups, in launches of up to max_tiles
+// groups; `ready` (may be null) makes them online: group k's tiles wait for
+// ready[k] == epoch (see StreamParams::ready).
+static int group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                           int B, int d, int64_t vocab_offset, int64_t G, int n_groups, float temperature,
+                           uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm, const uint32_t* ready,
+                           uint32_t epoch, uint64_t wait_ticks, int32_t* status, fs_group_summary_t* out, int path) {
   if (vocab_offset < 0 || vocab_offset % 32 != 0)
     return fail(FS_ERR_INVALID_ARG, "vocab_offset=%lld must be a non-negative multiple of 32", (long long)vocab_offset);
   if (n_groups < 1) return fail(FS_ERR_INVALID_ARG, "n_groups=%d must be >= 1", n_groups);
@@ -728,12 +732,38 @@ int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh
     p.n_tiles = (int)(tpg * ng);
     p.n_mblocks = gblocks * ng;
     p.group_out_stride = B;
+    p.ready = ready ? ready + g0 : nullptr;
+    p.ready_epoch = epoch;
+    p.wait_ticks = wait_ticks;
+    p.status = status;
     rc = run_stream_chunks(ctx, p, path, fsk::EPI_GROUP, (hipStream_t)stream, [&](fsk::StreamParams& c, int r0) {
       c.out_sum = reinterpret_cast<fsk::GroupSummary*>(out + (int64_t)g0 * B + r0);
     });
     if (rc != FS_OK) return rc;
   }
   return FS_OK;
+}
+
+int fs_group_summaries(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W, int64_t ldw,
+                       int B, int d, int64_t vocab_offset, int64_t G, int n_groups, float temperature, uint64_t seed,
+                       uint64_t step, const uint32_t* mask, int64_t ldm, fs_group_summary_t* out, int path) {
+  return group_summaries(ctx, stream, H, ldh, W, ldw, B, d, vocab_offset, G, n_groups, temperature, seed, step, mask,
+                         ldm, nullptr, 0, 0, nullptr, out, path);
+}
+
+int fs_group_summaries_online(fs_ctx* ctx, void* stream, const uint16_t* H, int64_t ldh, const uint16_t* W,
+                              int64_t ldw, int B, int d, int64_t vocab_offset, int64_t G, int n_groups,
+                              float temperature, uint64_t seed, uint64_t step, const uint32_t* mask, int64_t ldm,
+                              const uint32_t* ready, uint32_t epoch, uint32_t max_wait_us, int32_t* status,
+                              fs_group_summary_t* out, int path) {
+  if (!ready || !status) return fail(FS_ERR_INVALID_ARG, "ready and status must be non-NULL");
+  if (max_wait_us > 60u * 1000u * 1000u) return fail(FS_ERR_INVALID_ARG, "max_wait_us=%u exceeds 60 s", max_wait_us);
+  // the wait is counted on the GPU's constant-rate real-time clock
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, ctx->device) != hipSuccess || khz <= 0)
+    return fail(FS_ERR_HIP, "cannot read the wall clock rate of device %d", ctx->device);
+  return group_summaries(ctx, stream, H, ldh, W, ldw, B, d, vocab_offset, G, n_groups, temperature, seed, step, mask,
+                         ldm, ready, epoch, (uint64_t)max_wait_us * (uint64_t)khz / 1000u, status, out, path);
 }
 
 int fs_group_combine(fs_ctx* ctx, void* stream, const fs_group_summary_t* s, int n_groups, int B, uint64_t seed,

@@ -73,6 +73,14 @@ struct StreamParams {
   int top_k;
   uint64_t* topk_cand;
   float top_p;  // EPI_TOPK: nucleus of the kept ids (1: all of them)
+  // Online grouped summaries (EPI_GROUP with group_tiles > 0): when ready is
+  // not null, the tiles of launch group g start once ready[g] == ready_epoch,
+  // waiting at most wait_ticks of the 100 MHz real-time clock; a tile that
+  // gives up sets *status to 1 and does no work.
+  const uint32_t* ready;
+  uint32_t ready_epoch;
+  uint64_t wait_ticks;
+  int32_t* status;
 };
 
 struct SampleParams {  // unfused second pass: sample from stored logits

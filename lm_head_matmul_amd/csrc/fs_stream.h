@@ -139,6 +139,35 @@ struct TileRange {
   int rounds;
 };
 
+// Online grouped summaries: true once this tile's group has been published
+// (ready[g] == ready_epoch, read with system-scope acquire loads, so a flag in
+// host memory or one written by another stream's work is seen), false if the
+// wait ran out (then *status is set).  Thread 0 polls, sleeping between reads;
+// the barrier hands its answer, and the acquire's ordering, to the workgroup.
+// [arXiv 2603.15854 abstract: grouped variants for online settings; readus.org
+// FlashSampling summary, "Group Gumbel Max": the groups stream past, each one
+// summarized as it comes]
+__device__ __forceinline__ bool group_published(const StreamParams& p) {
+  __shared__ int ok;
+  if (threadIdx.x == 0) {
+    const int g = (int)(blockIdx.x / (unsigned)p.group_tiles);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    int r = 0;
+    for (;;) {
+      if (__hip_atomic_load(p.ready + g, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == p.ready_epoch) {
+        r = 1;
+        break;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > p.wait_ticks) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (!r) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    ok = r;
+  }
+  __syncthreads();
+  return ok != 0;
+}
+
 __device__ __forceinline__ TileRange tile_range(const StreamParams& p) {
   TileRange t;
   if (p.group_tiles > 0) {  // balanced inside each group
@@ -910,6 +939,10 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
                          : EPI == EPI_TOPK ? kLayoutTopk
                          : NOISE_LDS       ? kLayoutTable
                                            : kLayoutEpilogue;
+  if constexpr (EPI == EPI_GROUP) {
+    // the answer is the same in every lane; readfirstlane tells the compiler so
+    if (p.ready && !__builtin_amdgcn_readfirstlane((int)group_published(p))) return;
+  }
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -1082,6 +1115,10 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
 template <int NB, int EPI, bool MASKED, int RM>
 __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParams p) {
   constexpr int LAYOUT = EPI == EPI_TOPK ? kLayoutKouterTopk : kLayoutKouter;
+  if constexpr (EPI == EPI_GROUP) {
+    // the answer is the same in every lane; readfirstlane tells the compiler so
+    if (p.ready && !__builtin_amdgcn_readfirstlane((int)group_published(p))) return;
+  }
   static_assert(kFastRingChunked == 2, "two sub-blocks per chunk, two register buffers");
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1644,6 +1681,10 @@ template <int BD, int EPI, bool RESIDENT, bool FAST, bool MASKED,
           int RING = (RESIDENT ? kFastRingResident : kFastRingChunked)>
 __global__ void __launch_bounds__(kThreads) fmms_dot_kernel(const StreamParams p) {
   static_assert(BD <= 2, "dot kernel handles at most 2 batch rows");
+  if constexpr (EPI == EPI_GROUP) {
+    // the answer is the same in every lane; readfirstlane tells the compiler so
+    if (p.ready && !__builtin_amdgcn_readfirstlane((int)group_published(p))) return;
+  }
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
