@@ -60,6 +60,8 @@ def parse_args():
                          "headline steps only, of the call --profile-op names")
     ap.add_argument("--profile-op", default="fused", choices=sorted(PROFILE_OPS),
                     help="the call a --profile run times: the fused sampler, the unfused comparator, or top-k")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC1_CSV", "PMC2_CSV"),
+                    help="write the profiles/ counter summary of a --profile run's two counter passes and exit")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the profiles/ summaries of a --profile run's rocprofv3 csv output (for the "
                          "--profile-op, --workload and --batch given) and exit")
@@ -117,7 +119,72 @@ def profile_cmds(op, workload, B):
                  f"-- python3 bench.py {a} --steps 5 --warmup 2",
         "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}_write -o write "
                  f"-- python3 bench.py {a} --steps 5 --warmup 2",
+        "pmc1": f"rocprofv3 --pmc {' '.join(COUNTER_PASSES[0])} --output-format csv -d {d}_pmc1 -o pmc "
+                f"-- python3 bench.py {a} --steps 5 --warmup 2",
+        "pmc2": f"rocprofv3 --pmc {' '.join(COUNTER_PASSES[1])} --output-format csv -d {d}_pmc2 -o pmc "
+                f"-- python3 bench.py {a} --steps 5 --warmup 2",
     }
+
+
+# Two counter passes (each within one pass's limits: 8 SQ, 2 TA, 4 TCP counters) for the
+# streaming kernel's memory pipeline: how busy the address unit is and how often the L1 (TCP) holds
+# it up, the L1-to-L2 requests and their latency, MFMA and VALU activity.
+COUNTER_PASSES = (
+    ("SQ_BUSY_CYCLES", "SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VMEM_RD", "SQ_LDS_BANK_CONFLICT", "TA_TA_BUSY_sum",
+     "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum",
+     "TCP_PENDING_STALL_CYCLES_sum", "TCP_TCR_TCP_STALL_CYCLES_sum"),
+    ("GRBM_GUI_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_LDS", "SQ_INST_LEVEL_VMEM", "TA_FLAT_READ_LDS_WAVEFRONTS_sum",
+     "TA_DATA_STALLED_BY_TC_CYCLES_sum", "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TCP_TA_DATA_STALL_CYCLES_sum"),
+)
+
+
+def summarize_counters(pmc_csvs, op="fused", workload="mid_decode", B=64):
+    """The streaming kernel's counters (averaged over its calls) from the two counter passes of a
+    --profile run, with the figures they give: address-unit busy and held-up fractions, L1-to-L2
+    read requests per CU per clock and their mean latency."""
+    import csv
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    tag = f"{op}_{workload}_B{B}"
+    cmds = profile_cmds(op, workload, B)
+    per = {}
+    for fn in pmc_csvs:
+        for r in csv.DictReader(open(fn)):
+            if "fsk::" not in r["Kernel_Name"]:
+                continue
+            k = r["Kernel_Name"].split("(")[0]
+            d = per.setdefault(k, {"_n": set(), "_dur": []})
+            d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            d["_dur"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    stream = max(per, key=lambda k: sum(per[k]["_dur"]) / len(per[k]["_dur"]))
+    c = {k: sum(v) / len(v) for k, v in per[stream].items() if not k.startswith("_")}
+    n_cu, n_xcd = 256, 8  # MI355X; GRBM_GUI_ACTIVE adds up the busy clocks of the 8 XCDs
+    dur_us = sum(per[stream]["_dur"]) / len(per[stream]["_dur"]) / 1e3
+    gui = c.get("GRBM_GUI_ACTIVE")
+    gui = gui / n_xcd if gui else None
+    lines = [f"# {op}: {workload} head (B={B}, d={w['d']}, V={w['V']}), streaming-kernel counters", "",
+             f"counter pass 1: `cd /tmp && export TMPDIR=/tmp && cd <repo root> && {cmds['pmc1']}`", "",
+             f"counter pass 2: `cd /tmp && export TMPDIR=/tmp && cd <repo root> && {cmds['pmc2']}`", "",
+             f"Kernel: `{stream}`; every value is the average over its calls in the pass (the `_sum` counters "
+             "summed over the chip's instances).", "", "| counter | average per call |", "|---|---:|"]
+    for k in sorted(c):
+        lines.append(f"| {k} | {c[k]:.4g} |")
+    lines.append("")
+    if gui:
+        ta = c.get("TA_TA_BUSY_sum", 0) / (gui * n_cu)
+        stall = c.get("TA_ADDR_STALLED_BY_TC_CYCLES_sum", 0) / max(c.get("TA_TA_BUSY_sum", 1), 1)
+        req = c.get("TCP_TCC_READ_REQ_sum", 0)
+        lat = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0) / max(req, 1)
+        lines += [f"- busy clocks per call (GRBM_GUI_ACTIVE / {n_xcd} XCDs): {gui:.0f} in {dur_us:.1f} us of kernel "
+                  f"time in these passes ({gui / dur_us / 1e3:.2f} GHz)",
+                  f"- address unit (TA) busy: {ta * 100:.1f}% of those clocks per CU; held up by the L1 (TC) in "
+                  f"{stall * 100:.1f}% of its busy clocks",
+                  f"- L1-to-L2 read requests: {req:.4g} per call ({req * 128 / 1e6:.0f} MB at 128 B), "
+                  f"{req / (gui * n_cu):.3f} per CU per clock, mean latency {lat:.0f} clocks"]
+    open(os.path.join(ROOT, "profiles", f"{tag}_counters.md"), "w").write("\n".join(lines) + "\n")
+    print(f"wrote the {tag} counter summary ({stream})")
 
 
 def summarize_profiles(trace_csv, fetch_csv, write_csv, op="fused", workload="mid_decode", B=64):
@@ -269,6 +336,9 @@ def main():
     args = parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, op=args.profile_op, workload=args.workload, B=args.batch)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, op=args.profile_op, workload=args.workload, B=args.batch)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the sampler runs on one GPU: --gpus must be 1", "n_gpus": args.gpus}),
