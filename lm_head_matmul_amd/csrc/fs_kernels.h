@@ -162,7 +162,8 @@ constexpr int kFastRingChunked = 2;   // ... and with k-chunked H (chunks of exa
 constexpr int kMfmaMaxB = 64;
 // The wide kernel (65 .. kWideMaxB batch rows of the plain sampler, no mask):
 // kWideWaves waves, each holding wide_mw(NB) x NB accumulator blocks (NB = 8
-// up to 128 rows, 16 above); passes of up to kWideWaves * wide_mw(NB) vocab
+// up to 128 rows, 16 above; at NB = 16 the 80 blocks take all 256 AGPRs and
+// 64 VGPRs); passes of up to kWideWaves * wide_mw(NB) vocab
 // blocks; H in k-chunks of 32 wide_ksteps(NB), kWideHBufs LDS buffers of
 // wide_bufbytes(NB); W register items of one chunk, wide_ring(NB) of them,
 // each item's loads issued wide_lead(NB) chunks ahead (d must be a multiple
@@ -171,7 +172,7 @@ constexpr int kWideMaxB = 256;
 constexpr int kWideWaves = 4;
 constexpr int kWideHBufs = 3;
 constexpr int wide_nb(int B) { return B <= 128 ? 8 : 16; }
-constexpr int wide_mw(int nb) { return nb == 16 ? 4 : 5; }
+constexpr int wide_mw(int nb) { return 5; }
 constexpr int wide_ksteps(int nb) { return 2; }
 constexpr int wide_pieces(int nb) { return wide_ksteps(nb) * 4 + 1; }
 constexpr int wide_bufbytes(int nb) { return nb * 16 * wide_pieces(nb) * 16; }

@@ -374,9 +374,12 @@ __device__ __forceinline__ uint32_t mask_bits4(const StreamParams& p, const uint
 // order of a lane is increasing in v, so a strict comparison keeps the lowest
 // id on ties.
 // Gumbel noise of the four consecutive vocab ids gv0 .. gv0+3 (gv0 % 4 == 0,
-// global ids) of batch row b of the launch: one Philox call.
+// global ids) of batch row b of the launch: one Philox call.  MULTI = false
+// for kernels that only run launches of one sample per row (the row is then
+// row_offset + b, with no division).
+template <bool MULTI = true>
 __device__ __forceinline__ f32x4_t noise_quad(const StreamParams& p, int gv0, int b) {
-  const VRow v = vrow_of(p, b);
+  const VRow v = MULTI ? vrow_of(p, b) : VRow{b, (uint32_t)(p.row_offset + b), p.step_lo, p.step_hi};
   const Philox4 r = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)gv0 >> 2, v.row, v.step_lo, v.step_hi);
   return f32x4_t{gumbel_from_bits(r.w[0]), gumbel_from_bits(r.w[1]), gumbel_from_bits(r.w[2]),
                  gumbel_from_bits(r.w[3])};
@@ -1340,17 +1343,20 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
 // Wide kernel: 65 .. 256 batch rows of the plain sampler in one pass over W.
 // At these batch sizes each W byte carries 4 to 16 times the MFMA work of a
 // decode step, and operand reuse in registers decides the speed: a wave keeps
-// a 64 x 16 NB block of logits in accumulators (4 vocab blocks of 16 rows
+// an 80 x 16 NB block of logits in accumulators (5 vocab blocks of 16 rows
 // against NB batch blocks of 16 columns), so every W fragment feeds NB MFMAs
-// and every H fragment read from LDS feeds four.  At 256 rows and the MFMA
-// peak that is 64 bytes per clock of LDS reads and 16 of W loads per CU.
-// Four waves, one per SIMD (the accumulators take up to 256 registers), run
-// passes of 16 vocab blocks over the tile: a full pass gives each wave four
-// blocks; the tile's last pass spreads what is left over the waves (missing
-// block slots skip their MFMAs).  H comes through LDS in k-chunks of 32 KSTEPS,
-// three buffers, copied straight from global memory; W goes straight into
-// registers, each chunk's item two chunks ahead of its MFMAs.  The chunk order
-// is rotated per workgroup, as in the chunk-outer kernel.
+// and every H fragment read from LDS feeds five.  At 256 rows and the MFMA
+// peak that is about 51 bytes per clock of LDS reads and 16 of W loads per CU.
+// Four waves, one per SIMD (the accumulators take up to 320 registers: all
+// 256 AGPRs and 64 VGPRs at 256 rows), run passes of up to 20 vocab blocks:
+// the tile's blocks are split into as few near-equal passes as that allows
+// (a tile of 37 blocks: two), each wave taking a quarter of a pass (block
+// slots past a wave's count compute on repeated rows and are discarded).
+// Every pass reads all of H again, so the passes per tile set the H traffic.
+// H comes through LDS in k-chunks of 32 KSTEPS, three buffers, copied
+// straight from global memory; W goes straight into registers, each chunk's
+// item two chunks ahead of its MFMAs.  The chunk order is rotated per
+// workgroup, as in the chunk-outer kernel.
 // ---------------------------------------------------------------------------
 template <int NB>
 struct WideGeom {
@@ -1418,6 +1424,21 @@ struct WideItem {
   uint32_t off[MW];
 };
 
+// One 16x16x32 bf16 MFMA, acc += a * b, written in assembly with its
+// accumulator in AGPRs (ag, a constant after unrolling) or VGPRs.  The wide kernel's 80 accumulator
+// blocks at 256 rows need both register files; with the builtin, the compiler
+// gives every MFMA of a function accumulators of one class and copied the
+// rest across each chunk.  The compiler does not see these as MFMAs, so it
+// inserts no wait states for them: each accumulator is touched once per
+// chunk (dozens of MFMAs apart), and the kernel spaces the last MFMAs of a
+// pass from any vector instruction that reads their results (s_nop).
+__device__ __forceinline__ void mfma_bf16_asm(bool ag, f32x4_t& acc, const u32x4_t a, const u32x4_t b) {
+  if (ag)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
 // The MFMAs of one k-chunk, group by group (a group: one 32-wide k-step
 // against four batch blocks, for the wave's four vocab block slots), with the
 // vector-memory work of a later chunk spread over the groups: the copies of
@@ -1458,10 +1479,7 @@ __device__ __forceinline__ void wide_groups(const u32x4_t (&w)[wide_mw(NB)][wide
 #pragma unroll
     for (int m = 0; m < MW; ++m) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc[m][ng * 4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[m][e]),
-                                                                     __builtin_bit_cast(bf16x8_t, h[GI & 1][q]),
-                                                                     acc[m][ng * 4 + q], 0, 0, 0);
+      for (int q = 0; q < 4; ++q) mfma_bf16_asm(m * NB < 64, acc[m][ng * 4 + q], w[m][e], h[GI & 1][q]);
     }
     __builtin_amdgcn_sched_barrier(0);
     wide_groups<NB, GI + 1>(w, hb, acc, h, p, c3, hbuf3, hsrc, it, dst);
@@ -1570,11 +1588,16 @@ fmms_wide_kernel(const StreamParams p) {
   h_wide_offsets<NB>(p, hsrc);
   h_wide_dma<NB>(p, rot, smem, hsrc);
   h_wide_dma<NB>(p, rot + 1 < nchunk ? rot + 1 : 0, smem + G::BUFBYTES, hsrc);
+  // (in chunk order: the compiler's wait for an item's registers counts the
+  // loads issued after it)
 #pragma unroll
-  for (int j = 0; j < LEAD; ++j)
+  for (int j = 0; j < LEAD; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
     wide_wload<NB>(wide_item<NB>(p, mb_lo, mb_hi, npass, wave, off_full, off_delta, 0,
                                  rot + j < nchunk ? rot + j : rot + j - nchunk),
                    wb[j]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   int hcur = 0;  // LDS buffer of the current chunk (chunk t uses buffer t mod 3)
   for (int q = 0; q < npass; ++q) {
     int mb0, mw;
@@ -1603,6 +1626,10 @@ fmms_wide_kernel(const StreamParams p) {
                        smem + (hcur == 0 ? 2 : hcur - 1) * G::BUFBYTES, hsrc, it,          \
                        wb[((r) + LEAD) % RING]);                                           \
     hcur = hcur == 2 ? 0 : hcur + 1;                                                       \
+    if constexpr ((r) == RING - 1) { /* results read by vector code after the loop */     \
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");                          \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
   }
       // Each item t: everything but the last three batches issued (chunk
       // t + LEAD - 1's W item, chunk t + 2's copies, chunk t + LEAD's W item)
@@ -1629,11 +1656,13 @@ fmms_wide_kernel(const StreamParams p) {
   if constexpr ((m) < MW) {                                                                       \
     if ((m) < mw) {                                                                               \
       const int v0 = (int)((mb0 + (m)) * 16) + grp * 4;                                           \
+      int lb = l16; /* opaque here, so that no row's noise terms are kept across the pass */      \
+      asm volatile("" : "+v"(lb));                                                                \
       _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                         \
-        const int b = nb * 16 + l16;                                                              \
+        const int b = nb * 16 + lb;                                                               \
         if (b < p.B) {                                                                            \
           const float a4[4] = {acc[m][nb][0], acc[m][nb][1], acc[m][nb][2], acc[m][nb][3]};       \
-          const f32x4_t g = noise_quad(p, (int)(p.vocab_offset + v0), b);                         \
+          const f32x4_t g = noise_quad<false>(p, (int)(p.vocab_offset + v0), b);                  \
           epilogue_quad<EPI_FLAT>(p, v0, a4, g, 0xFu, bv[nb], bi[nb], lm[nb], ls[nb]);            \
         }                                                                                         \
         __builtin_amdgcn_sched_barrier(0); /* one quad's noise at a time (registers) */          \
