@@ -407,7 +407,7 @@ int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k)
   if (max_top_k > 0) {
     c->topk_rows = max_B < fsk::kMfmaMaxB ? max_B : fsk::kMfmaMaxB;
     c->topk_ldl = (max_V + 3) / 4 * 4;
-    const size_t lists = (size_t)c->topk_rows * c->max_tiles * fsk::kWaves * fsk::kTopkSlot * sizeof(uint64_t);
+    const size_t lists = (size_t)c->topk_rows * c->max_tiles * fsk::kTopkSlot * sizeof(uint64_t);
     e = hipMalloc(&c->topk_lists, lists);
     if (e == hipSuccess && max_top_k > fsk::kTopkFusedMax)
       e = hipMalloc(&c->topk_ws, (size_t)c->topk_rows * (size_t)c->topk_ldl * sizeof(float));

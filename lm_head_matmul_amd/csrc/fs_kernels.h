@@ -68,8 +68,8 @@ struct StreamParams {
   float* logits;  // EPI_STORE: [B][ldl] fp32
   int64_t ldl;
   int tile_ratio;  // 0: equal tiles; else XCD-weighted tiles (see tile_lo)
-  // EPI_TOPK: k, and the per-(row, tile, wave) candidate lists, laid out as
-  // topk_cand[((b * kWaves + wave) * kTopkSlot + j) * n_tiles + tile]
+  // EPI_TOPK: k, and the per-(row, tile) candidate lists, laid out as
+  // topk_cand[(b * kTopkSlot + j) * n_tiles + tile]
   int top_k;
   uint64_t* topk_cand;
   float top_p;  // EPI_TOPK: nucleus of the kept ids (1: all of them)
@@ -205,12 +205,16 @@ constexpr int kLayoutDot = 0;       // dot-product kernel
 constexpr int kouter_max_rounds(int epi, int nb, bool masked) {
   return (nb <= 2 || epi == EPI_STORE || ((epi == EPI_FLAT || epi == EPI_TOPK) && !masked)) ? 5 : 3;
 }
-// Fused top-k: each lane keeps its kTopkLane best (score, id) pairs; each wave
-// merges its lanes' lists per batch row into kTopkLane entries plus one bound
-// (kTopkSlot = kTopkLane + 1 words of the candidate buffer).  k up to
+// Fused top-k: each lane keeps its kTopkLane best (score, id) pairs; each
+// workgroup merges its lanes' lists per batch row into kTopkLane entries plus
+// one bound (kTopkSlot = kTopkLane + 1 words of the candidate buffer).  k up to
 // kTopkFusedMax runs fused; larger k stores the logits and selects from them.
 constexpr int kTopkLane = 4;
 constexpr int kTopkSlot = kTopkLane + 1;
+// LDS bytes the end of a top-k streaming kernel uses (the H buffers, free by
+// then): every wave's list and bound for each of the 16 NB batch columns, which
+// the workgroup merges into one list per tile.
+constexpr int topk_finish_lds(int nb) { return kWaves * nb * 16 * kTopkSlot * 8; }
 constexpr int kTopkFusedMax = 64;
 constexpr int kTopkMergeThreads = 256;
 constexpr int kTopkMergeCap = 4096;      // candidate keys a row's merge holds in LDS

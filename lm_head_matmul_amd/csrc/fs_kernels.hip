@@ -557,8 +557,8 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams
 }
 // ---------------------------------------------------------------------------
 // Fused top-k, second launch: one workgroup per batch row merges the lists the
-// streaming pass (EPI_TOPK) left per (tile, wave): kTopkLane keys and a bound
-// on the keys that wave dropped.  [readus.org FlashSampling summary, section on
+// streaming pass (EPI_TOPK) left per tile: kTopkLane keys and a bound on the
+// keys that tile dropped.  [readus.org FlashSampling summary, section on
 // Top-K and masking: a pre-filter keeps candidates, exact Gumbel-Max runs on
 // them]  Keys order (score desc, id asc); the row's top-k is the k largest.
 //   1. theta, a lower bound of the row's k-th key tau: each wave takes the
@@ -567,9 +567,9 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams
 //      distinct ids, at or above it.  Only list entries >= theta can be kept:
 //      they are gathered.  Without such a bound, or if it gathers more than
 //      32 k entries, theta is the k-th largest tile maximum itself (then at
-//      most 32 k entries reach it).
+//      most kTopkLane k entries reach it).
 //   2. tau = the k-th largest gathered key (0 = keep all if there are fewer).
-//   3. A wave whose bound reaches tau may have dropped a kept id.  Then its
+//   3. A tile whose bound reaches tau may have dropped a kept id.  Then the
 //      tile is rescored (every id of the tile recomputed from H and W in fp32)
 //      and the selection redone over the other tiles' lists and the rescored
 //      ids, with the threshold lowered by the near-tie margin so that another
@@ -577,7 +577,7 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams
 //      repeated until no unrescored tile's bound reaches tau.  On the decode
 //      workloads no bound comes near tau; ties and tiny vocabularies take it.
 //   4. Gumbel-max over the kept ids with the per-id noise of the plain sampler.
-// Thread t holds tile t's lists (n_tiles <= kTopkMergeThreads).
+// Thread t holds tile t's list (n_tiles <= kTopkMergeThreads).
 // ---------------------------------------------------------------------------
 static_assert(kTopkMergeThreads == 256 && kTopkMergeCap % kTopkMergeThreads == 0, "merge geometry");
 static_assert(kTopkFusedMax <= 64, "the nucleus cut sorts the kept keys within one wave");
@@ -756,28 +756,24 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
   const int nt = p.n_tiles, k = p.top_k;
   const bool has = tid < nt;
-  const uint64_t* cand = p.topk_cand + (int64_t)b * kWaves * kTopkSlot * nt;
+  const uint64_t* cand = p.topk_cand + (int64_t)b * kTopkSlot * nt;
   const uint32_t row = (uint32_t)(p.row_offset + b);
   auto noise_of = [&](int32_t id) {
     const Philox4 rr = philox4x32_10(p.seed_lo, p.seed_hi, (uint32_t)id >> 2, row, p.step_lo, p.step_hi);
     const uint32_t q = (uint32_t)id & 3u;
     return gumbel_from_bits(q == 0 ? rr.w[0] : q == 1 ? rr.w[1] : q == 2 ? rr.w[2] : rr.w[3]);
   };
-  uint64_t e[kWaves][kTopkLane], hb[kWaves];
+  // this thread's tile: its kTopkLane best keys (descending) and its bound
+  uint64_t e[kTopkLane];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-#pragma unroll
-    for (int j = 0; j < kTopkLane; ++j) e[w][j] = has ? cand[(int64_t)(w * kTopkSlot + j) * nt + tid] : 0ull;
-    hb[w] = has ? cand[(int64_t)(w * kTopkSlot + kTopkLane) * nt + tid] : 0ull;
-  }
+  for (int j = 0; j < kTopkLane; ++j) e[j] = has ? cand[(int64_t)j * nt + tid] : 0ull;
+  const uint64_t hb = has ? cand[(int64_t)kTopkLane * nt + tid] : 0ull;
   // 1. theta, a lower bound of the row's k-th key: in each wave the
   // ceil(k/4)-th largest score among its 64 tile maxima; at least k keys reach
   // the smallest of the four, so every key with at least that score is gathered.
   // If a wave holds fewer keys, or the bound gathers more than 32 k entries,
   // theta is the k-th largest tile maximum itself (ranks by counting over LDS).
-  uint64_t x = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) x = e[w][0] > x ? e[w][0] : x;
+  const uint64_t x = e[0];
   sh.S[tid] = x;
   sh.rescored[tid] = 0;
   if (tid == 0) {
@@ -800,21 +796,17 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
   int cnt = 0;
   if (t32 != 0) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int j = 0; j < kTopkLane; ++j) cnt += e[w][j] >= th ? 1 : 0;
+    for (int j = 0; j < kTopkLane; ++j) cnt += e[j] >= th ? 1 : 0;
     int at = cnt > 0 ? atomicAdd(&sh.nF, cnt) : 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int j = 0; j < kTopkLane; ++j)
-        if (e[w][j] >= th) {
-          if (at < kTopkMergeCap) {
-            sh.F[at] = e[w][j];
-            sh.Ft[at] = (uint16_t)tid;
-          }
-          ++at;
+    for (int j = 0; j < kTopkLane; ++j)
+      if (e[j] >= th) {
+        if (at < kTopkMergeCap) {
+          sh.F[at] = e[j];
+          sh.Ft[at] = (uint16_t)tid;
         }
+        ++at;
+      }
   }
   __syncthreads();
   if (t32 == 0 || sh.nF > 32 * k) {
@@ -826,19 +818,15 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
     __syncthreads();
     cnt = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int j = 0; j < kTopkLane; ++j) cnt += e[w][j] >= th ? 1 : 0;
+    for (int j = 0; j < kTopkLane; ++j) cnt += e[j] >= th ? 1 : 0;
     int at = cnt > 0 ? atomicAdd(&sh.nF, cnt) : 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int j = 0; j < kTopkLane; ++j)
-        if (e[w][j] >= th) {
-          sh.F[at] = e[w][j];
-          sh.Ft[at] = (uint16_t)tid;
-          ++at;
-        }
+    for (int j = 0; j < kTopkLane; ++j)
+      if (e[j] >= th) {
+        sh.F[at] = e[j];
+        sh.Ft[at] = (uint16_t)tid;
+        ++at;
+      }
     __syncthreads();
   }
   // 2. tau: the k-th largest gathered key (0 if fewer than k), by ranks
@@ -848,10 +836,7 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
   // 3. a tile whose dropped keys could reach tau is rescored
   __syncthreads();
   uint64_t tau = sh.tau;
-  bool flag = false;
-  if (has)
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) flag |= hb[w] != 0 && hb[w] >= tau;
+  bool flag = has && hb != 0 && hb >= tau;
   if (flag) {
     sh.rescored[tid] = 1;
     atomicAdd(&sh.nnew, 1);
@@ -867,10 +852,9 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
       __syncthreads();
       if (tid == 0) sh.nF = 0;
       const bool mine = has && !sh.rescored[tid];
-#pragma unroll 1
-      for (int q = 0; q < kWaves * kTopkLane; ++q) {  // this path reads the lists again from memory
-        const int w = q / kTopkLane, j = q - w * kTopkLane;
-        const uint64_t v = mine ? cand[(int64_t)(w * kTopkSlot + j) * nt + tid] : 0ull;
+#pragma unroll
+      for (int j = 0; j < kTopkLane; ++j) {
+        const uint64_t v = mine ? e[j] : 0ull;
         topk_append(sh, v >= th2 ? v : 0ull, tid, k);
       }
 #pragma unroll 1
@@ -897,10 +881,7 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
       tau = topk_select_kth(sh, k);
       if (tid == 0) sh.nnew = 0;
       __syncthreads();
-      flag = false;
-      if (has && !sh.rescored[tid])
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) flag |= hb[w] != 0 && hb[w] >= tau;
+      flag = has && !sh.rescored[tid] && hb != 0 && hb >= tau;
       if (flag) {
         sh.rescored[tid] = 1;
         atomicAdd(&sh.nnew, 1);
@@ -1282,7 +1263,7 @@ bool plan_stream(StreamParams& p, StreamConfig& cfg, int epi) {
   const int hr = cfg.dot ? cfg.bd : (p.B < Bp ? p.B + 1 : Bp);
   p.h_rows = hr;
   p.nsub = (p.d + 255) / 256;
-  const int scratch = kWaves * Bp * 16;
+  const int scratch = epi == EPI_TOPK ? topk_finish_lds(cfg.nb) : kWaves * Bp * 16;
   auto rowstride = [](int cs) { return cs * 512 + 16; };
   const int64_t tile_rows = 16 * ((p.n_mblocks + p.n_tiles - 1) / p.n_tiles);  // largest tile
   // mask words of the largest tile (tile rows are a whole number of 16-row blocks)

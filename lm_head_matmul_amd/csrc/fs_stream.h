@@ -431,9 +431,9 @@ __device__ __forceinline__ void epilogue_quad(const StreamParams& p, int v0, con
 // part's own top-k, for any partition of the vocabulary; a part that keeps
 // fewer entries is still exact as long as everything it dropped ranks below
 // the row's k-th kept score.  So each lane keeps its kTopkLane best (score,
-// id) pairs and counts what it saw; a wave merges its lanes' lists per
-// batch row into kTopkLane entries plus a bound on every dropped key, which
-// the merge kernel checks against the row's k-th key (and recomputes the
+// id) pairs and counts what it saw; the workgroup merges its lanes' lists
+// per batch row into kTopkLane entries plus a bound on every dropped key,
+// which the merge kernel checks against the row's k-th key (and recomputes the
 // tile's ids where the check fails).
 // ---------------------------------------------------------------------------
 struct TopkList {
@@ -471,16 +471,48 @@ __device__ __forceinline__ void topk_push(TopkList& t, float s, int32_t id) {
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t u64_min(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// End of a top-k streaming kernel: per batch column, merge the four lane
-// groups' lists of a wave (lanes l16, l16 + 16, l16 + 32, l16 + 48) and write
-// the wave's kTopkLane best keys and its bound -- the largest key it may have
-// dropped (0 if none) -- to the candidate buffer.  Two sorted lists of four
-// merge by one step of a bitonic merge: the elementwise maxima of one list and
-// the other reversed are the best four, the minima the four dropped.
+// Two sorted lists of four keys (k: this lane's, the partner lane's at lane
+// distance `off`) and bounds h on what each dropped: afterwards k is the best
+// four of both, descending, and h bounds everything dropped (the larger bound
+// and the best key of the four not kept).  One step of a bitonic merge: the
+// elementwise maxima of one list and the other reversed are the best four, the
+// minima the four dropped.
+__device__ __forceinline__ void topk_merge_lists(uint64_t (&k)[kTopkLane], uint64_t& h, int off) {
+  static_assert(kTopkLane == 4, "the merge below is written for four entries");
+  uint64_t q[kTopkLane];
+#pragma unroll
+  for (int j = 0; j < kTopkLane; ++j) q[j] = __shfl_xor(k[j], off);
+  h = u64_max(h, __shfl_xor(h, off));
+  uint64_t top[kTopkLane];
+#pragma unroll
+  for (int j = 0; j < kTopkLane; ++j) {
+    top[j] = u64_max(k[j], q[kTopkLane - 1 - j]);
+    h = u64_max(h, u64_min(k[j], q[kTopkLane - 1 - j]));
+  }
+  // top is bitonic: two compare-exchange stages sort it descending
+  const uint64_t a0 = u64_max(top[0], top[2]), a2 = u64_min(top[0], top[2]);
+  const uint64_t a1 = u64_max(top[1], top[3]), a3 = u64_min(top[1], top[3]);
+  k[0] = u64_max(a0, a1);
+  k[1] = u64_min(a0, a1);
+  k[2] = u64_max(a2, a3);
+  k[3] = u64_min(a2, a3);
+}
+
+// End of a top-k streaming kernel: per batch column, each wave merges its four
+// lane groups' lists (lanes l16, l16 + 16, l16 + 32, l16 + 48); the waves'
+// lists meet in LDS, where eight lanes per column merge the workgroup's eight
+// into the tile's kTopkLane best keys and its bound -- the largest key it may
+// have dropped (0 if none) -- which one lane writes to the candidate buffer.
+// One list per tile keeps the buffer (and the merge launch's reads) an eighth
+// of per-wave lists, and the write of a column's five words is one request per
+// word instead of one per wave and word.
 template <int NB>
-__device__ __forceinline__ void finish_wave_topk(const StreamParams& p, TopkList (&tk)[NB]) {
+__device__ __forceinline__ void finish_wave_topk(const StreamParams& p, unsigned char* smem, TopkList (&tk)[NB]) {
+  constexpr int Bp = NB * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
+  __syncthreads();  // H buffers are free: reuse LDS as scratch
+  uint64_t* sl = (uint64_t*)smem;  // [wave][column][kTopkSlot]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     uint64_t k[kTopkLane];
@@ -488,29 +520,30 @@ __device__ __forceinline__ void finish_wave_topk(const StreamParams& p, TopkList
     for (int j = 0; j < kTopkLane; ++j) k[j] = tk[nb].id[j] >= 0 ? topk_key(tk[nb].s[j], tk[nb].id[j]) : 0ull;
     // whatever the lane dropped ranks below its last entry (keys are distinct)
     uint64_t h = tk[nb].seen > kTopkLane && k[kTopkLane - 1] != 0 ? k[kTopkLane - 1] - 1 : 0ull;
+    topk_merge_lists(k, h, 16);
+    topk_merge_lists(k, h, 32);
+    if (grp == 0) {
+      uint64_t* d = sl + (wave * Bp + nb * 16 + l16) * kTopkSlot;
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      uint64_t q[kTopkLane];
-#pragma unroll
-      for (int j = 0; j < kTopkLane; ++j) q[j] = __shfl_xor(k[j], off);
-      h = u64_max(h, __shfl_xor(h, off));
-      uint64_t top[kTopkLane];
-#pragma unroll
-      for (int j = 0; j < kTopkLane; ++j) {
-        top[j] = u64_max(k[j], q[kTopkLane - 1 - j]);
-        h = u64_max(h, u64_min(k[j], q[kTopkLane - 1 - j]));
-      }
-      // top is bitonic: two compare-exchange stages sort it descending
-      uint64_t a0 = u64_max(top[0], top[2]), a2 = u64_min(top[0], top[2]);
-      uint64_t a1 = u64_max(top[1], top[3]), a3 = u64_min(top[1], top[3]);
-      k[0] = u64_max(a0, a1);
-      k[1] = u64_min(a0, a1);
-      k[2] = u64_max(a2, a3);
-      k[3] = u64_min(a2, a3);
+      for (int j = 0; j < kTopkLane; ++j) d[j] = k[j];
+      d[kTopkLane] = h;
     }
-    const int b = nb * 16 + l16;
-    if (grp == 0 && b < p.B) {
-      uint64_t* dst = p.topk_cand + ((int64_t)(b * kWaves + wave) * kTopkSlot) * p.n_tiles + blockIdx.x;
+  }
+  __syncthreads();
+  // thread t: column t / 8, wave t % 8's list (eight consecutive lanes of a wave)
+  static_assert(kWaves == 8 && kThreads >= 8 * 64, "eight lists per column, 64 columns at most");
+  const int b = (int)threadIdx.x >> 3, w = (int)threadIdx.x & 7;
+  if (b < Bp) {  // uniform per wave: Bp is a multiple of 16
+    const uint64_t* s = sl + (w * Bp + b) * kTopkSlot;
+    uint64_t k[kTopkLane];
+#pragma unroll
+    for (int j = 0; j < kTopkLane; ++j) k[j] = s[j];
+    uint64_t h = s[kTopkLane];
+    topk_merge_lists(k, h, 1);
+    topk_merge_lists(k, h, 2);
+    topk_merge_lists(k, h, 4);
+    if (w == 0 && b < p.B) {
+      uint64_t* dst = p.topk_cand + (int64_t)b * kTopkSlot * p.n_tiles + blockIdx.x;
 #pragma unroll
       for (int j = 0; j < kTopkLane; ++j) dst[(int64_t)j * p.n_tiles] = k[j];
       dst[(int64_t)kTopkLane * p.n_tiles] = h;
@@ -1094,7 +1127,7 @@ __global__ void __launch_bounds__(kThreads) fmms_mfma_kernel(const StreamParams 
   }
   if (EPI == EPI_STORE) return;
   if (EPI == EPI_TOPK) {
-    finish_wave_topk<NB>(p, tk);
+    finish_wave_topk<NB>(p, smem, tk);
     return;
   }
   finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
@@ -1333,7 +1366,7 @@ __global__ void __launch_bounds__(kThreads) fmms_kouter_kernel(const StreamParam
   }
   if (EPI == EPI_STORE) return;
   if (EPI == EPI_TOPK) {
-    finish_wave_topk<NB>(p, tk);
+    finish_wave_topk<NB>(p, smem, tk);
     return;
   }
   finish_wave_tile<EPI, NB>(p, smem, bv, bi, lm, ls);
