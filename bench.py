@@ -77,9 +77,12 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 def floors(B, d, V, mask=False):
     """Lower bounds of a step's time: streaming its algorithmic bytes at peak HBM bandwidth,
-    and its 2 B V d multiply-adds at the dense bf16 MFMA peak."""
+    and its 2 B V d multiply-adds at the dense bf16 MFMA peak; with them the step's noise work,
+    the vector-ALU side of the epilogue: one Gumbel value per (row, id), i.e. B V / 4
+    Philox4x32-10 calls (four words each) and two logarithms per value."""
     return {"hbm_floor_us": round(algorithmic_bytes(B, d, V, mask) / (PEAK_HBM_GBS * 1e3), 2),
-            "mfma_floor_us": round(2.0 * B * V * d / (PEAK_BF16_TFLOPS * 1e6), 2)}
+            "mfma_floor_us": round(2.0 * B * V * d / (PEAK_BF16_TFLOPS * 1e6), 2),
+            "noise_ops": {"gumbel_values": B * V, "philox4x32_10_calls": B * V // 4, "log_evals": 2 * B * V}}
 
 
 def kernel_source_hash():
@@ -485,6 +488,7 @@ def main():
                                                              else tr["unfused"] - tr["fused"]),
                      "algorithmic_bytes_per_launch": algo,
                      "kernel_us": round(kern_ms * 1e3, 2),
+                     "floors": floors(B, w["d"], w["V"]),
                      "note": "achieved = algorithmic bytes of one launch / the streaming kernel's mean duration "
                              "(HIP events around each launch, K steps right after the timed region); traffic = calibrated "
                              "FETCH_SIZE + WRITE_SIZE per launch from profiles/ (null if the kernels changed)"},
