@@ -471,18 +471,52 @@ __device__ __forceinline__ void topk_push(TopkList& t, float s, int32_t id) {
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t u64_min(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
+// x from lane (lane ^ OFF) of the wave, OFF in {1, 2, 4, 16, 32}, on the
+// vector ALU: DPP moves within a row of 16 lanes (quad permutes for 1 and 2,
+// row shifts either way for 4) and gfx950's permlane swaps across rows (for
+// 16 and 32: one swap of x with itself leaves lane l's partner in one of the
+// two results).  __shfl_xor goes through the LDS crossbar, a round trip per
+// exchange, and the list merges below are chains of exchanges.  Every lane of
+// the wave must be active.
+template <int OFF>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (OFF == 1) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (OFF == 2) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (OFF == 4) {
+    const uint32_t up = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0xF, false);  // row_shl:4 (from lane + 4)
+    const uint32_t dn = __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4 (from lane - 4)
+    return (lane & 4) ? dn : up;
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(OFF == 32, "lane distances 1, 2, 4, 16 and 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+template <int OFF>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x) {
+  return (uint64_t)lane_xor<OFF>((uint32_t)x) | ((uint64_t)lane_xor<OFF>((uint32_t)(x >> 32)) << 32);
+}
+
 // Two sorted lists of four keys (k: this lane's, the partner lane's at lane
-// distance `off`) and bounds h on what each dropped: afterwards k is the best
+// distance OFF) and bounds h on what each dropped: afterwards k is the best
 // four of both, descending, and h bounds everything dropped (the larger bound
 // and the best key of the four not kept).  One step of a bitonic merge: the
 // elementwise maxima of one list and the other reversed are the best four, the
 // minima the four dropped.
-__device__ __forceinline__ void topk_merge_lists(uint64_t (&k)[kTopkLane], uint64_t& h, int off) {
+template <int OFF>
+__device__ __forceinline__ void topk_merge_lists(uint64_t (&k)[kTopkLane], uint64_t& h) {
   static_assert(kTopkLane == 4, "the merge below is written for four entries");
   uint64_t q[kTopkLane];
 #pragma unroll
-  for (int j = 0; j < kTopkLane; ++j) q[j] = __shfl_xor(k[j], off);
-  h = u64_max(h, __shfl_xor(h, off));
+  for (int j = 0; j < kTopkLane; ++j) q[j] = lane_xor64<OFF>(k[j]);
+  h = u64_max(h, lane_xor64<OFF>(h));
   uint64_t top[kTopkLane];
 #pragma unroll
   for (int j = 0; j < kTopkLane; ++j) {
@@ -520,8 +554,8 @@ __device__ __forceinline__ void finish_wave_topk(const StreamParams& p, unsigned
     for (int j = 0; j < kTopkLane; ++j) k[j] = tk[nb].id[j] >= 0 ? topk_key(tk[nb].s[j], tk[nb].id[j]) : 0ull;
     // whatever the lane dropped ranks below its last entry (keys are distinct)
     uint64_t h = tk[nb].seen > kTopkLane && k[kTopkLane - 1] != 0 ? k[kTopkLane - 1] - 1 : 0ull;
-    topk_merge_lists(k, h, 16);
-    topk_merge_lists(k, h, 32);
+    topk_merge_lists<16>(k, h);
+    topk_merge_lists<32>(k, h);
     if (grp == 0) {
       uint64_t* d = sl + (wave * Bp + nb * 16 + l16) * kTopkSlot;
 #pragma unroll
@@ -539,9 +573,9 @@ __device__ __forceinline__ void finish_wave_topk(const StreamParams& p, unsigned
 #pragma unroll
     for (int j = 0; j < kTopkLane; ++j) k[j] = s[j];
     uint64_t h = s[kTopkLane];
-    topk_merge_lists(k, h, 1);
-    topk_merge_lists(k, h, 2);
-    topk_merge_lists(k, h, 4);
+    topk_merge_lists<1>(k, h);
+    topk_merge_lists<2>(k, h);
+    topk_merge_lists<4>(k, h);
     if (w == 0 && b < p.B) {
       uint64_t* dst = p.topk_cand + (int64_t)b * kTopkSlot * p.n_tiles + blockIdx.x;
 #pragma unroll
