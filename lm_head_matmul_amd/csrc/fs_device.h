@@ -99,6 +99,47 @@ __device__ __forceinline__ float gumbel_from_bits(uint32_t r) {
   return -fast_ln(e);
 }
 
+// x from lane (lane ^ OFF) of the wave, OFF a power of two up to 32, on the
+// vector ALU: DPP moves within a row of 16 lanes (quad permutes for 1 and 2,
+// row shifts either way for 4, a rotation by half a row for 8) and gfx950's
+// permlane swaps across rows (for 16 and 32: one swap of x with itself leaves
+// lane l's partner in one of the two results).  __shfl_xor goes through the
+// LDS crossbar, a round trip per exchange, and the reductions and list merges
+// at the end of a tile are chains of exchanges.  Every lane of the wave must
+// be active.
+template <int OFF>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (OFF == 1) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (OFF == 2) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (OFF == 4) {
+    const uint32_t up = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0xF, false);  // row_shl:4 (from lane + 4)
+    const uint32_t dn = __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4 (from lane - 4)
+    return (lane & 4) ? dn : up;
+  } else if constexpr (OFF == 8) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(OFF == 32, "lane distances 1, 2, 4, 8, 16 and 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+template <int OFF>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x) {
+  return (uint64_t)lane_xor<OFF>((uint32_t)x) | ((uint64_t)lane_xor<OFF>((uint32_t)(x >> 32)) << 32);
+}
+
+template <int OFF>
+__device__ __forceinline__ float lane_xor_f(float x) {
+  return __uint_as_float(lane_xor<OFF>(__float_as_uint(x)));
+}
+
 // ---------------------------------------------------------------------------
 // (value, index) maximizer with the lowest-index tie rule.  NaN values never
 // win: they fail every comparison.

@@ -32,6 +32,18 @@
 
 namespace fsk {
 
+// One butterfly step at lane distance OFF of the (value, index) maximizer and,
+// grouped, of the log-sum-exp state: each lane merges its partner's (both
+// merges are symmetric, so the pair ends equal).
+template <int EPI, int OFF>
+__device__ __forceinline__ void best_step(float& v, int32_t& i, float& m, float& s) {
+  merge_best(v, i, lane_xor_f<OFF>(v), (int32_t)lane_xor<OFF>((uint32_t)i));
+  if (EPI == EPI_GROUP) {
+    const float om = lane_xor_f<OFF>(m), os = lane_xor_f<OFF>(s);
+    lse_merge(m, s, om, os);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cross-tile reduction: a second, small launch on the same stream (the kernel
 // boundary publishes the workspace), one wave per batch row over its n_tiles
@@ -80,17 +92,12 @@ __global__ void __launch_bounds__(kThreads)
       if (EPI == EPI_GROUP) lse_merge(m, s, mm[u], ss[u]);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off);
-    const int32_t oi = __shfl_xor(i, off);
-    merge_best(v, i, ov, oi);
-    if (EPI == EPI_GROUP) {
-      const float om = __shfl_xor(m, off);
-      const float os = __shfl_xor(s, off);
-      lse_merge(m, s, om, os);
-    }
-  }
+  best_step<EPI, 32>(v, i, m, s);
+  best_step<EPI, 16>(v, i, m, s);
+  best_step<EPI, 8>(v, i, m, s);
+  best_step<EPI, 4>(v, i, m, s);
+  best_step<EPI, 2>(v, i, m, s);
+  best_step<EPI, 1>(v, i, m, s);
   if (lane == 0) {
     if (EPI == EPI_GROUP) {
       GroupSummary g;
@@ -470,39 +477,6 @@ __device__ __forceinline__ void topk_push(TopkList& t, float s, int32_t id) {
 
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t u64_min(uint64_t a, uint64_t b) { return a < b ? a : b; }
-
-// x from lane (lane ^ OFF) of the wave, OFF in {1, 2, 4, 16, 32}, on the
-// vector ALU: DPP moves within a row of 16 lanes (quad permutes for 1 and 2,
-// row shifts either way for 4) and gfx950's permlane swaps across rows (for
-// 16 and 32: one swap of x with itself leaves lane l's partner in one of the
-// two results).  __shfl_xor goes through the LDS crossbar, a round trip per
-// exchange, and the list merges below are chains of exchanges.  Every lane of
-// the wave must be active.
-template <int OFF>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (OFF == 1) {
-    return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  } else if constexpr (OFF == 2) {
-    return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (OFF == 4) {
-    const uint32_t up = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0xF, false);  // row_shl:4 (from lane + 4)
-    const uint32_t dn = __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4 (from lane - 4)
-    return (lane & 4) ? dn : up;
-  } else if constexpr (OFF == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    static_assert(OFF == 32, "lane distances 1, 2, 4, 16 and 32");
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
-
-template <int OFF>
-__device__ __forceinline__ uint64_t lane_xor64(uint64_t x) {
-  return (uint64_t)lane_xor<OFF>((uint32_t)x) | ((uint64_t)lane_xor<OFF>((uint32_t)(x >> 32)) << 32);
-}
 
 // Two sorted lists of four keys (k: this lane's, the partner lane's at lane
 // distance OFF) and bounds h on what each dropped: afterwards k is the best
@@ -955,17 +929,8 @@ __device__ __forceinline__ void finish_wave_tile(const StreamParams& p, unsigned
   const int l16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float ov = __shfl_xor(bv[nb], off);
-      const int32_t oi = __shfl_xor(bi[nb], off);
-      merge_best(bv[nb], bi[nb], ov, oi);
-      if (EPI == EPI_GROUP) {
-        const float om = __shfl_xor(lm[nb], off);
-        const float os = __shfl_xor(ls[nb], off);
-        lse_merge(lm[nb], ls[nb], om, os);
-      }
-    }
+    best_step<EPI, 16>(bv[nb], bi[nb], lm[nb], ls[nb]);
+    best_step<EPI, 32>(bv[nb], bi[nb], lm[nb], ls[nb]);
   }
   __syncthreads();  // H buffers are free: reuse LDS as scratch
   float* sv = (float*)smem;
