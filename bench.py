@@ -700,6 +700,26 @@ def main():
                                   "per_row_seconds_min_median_max": [round(per_row[0], 4),
                                                                      round(per_row[len(per_row) // 2], 4),
                                                                      round(per_row[-1], 4)]}
+        # the tiny configuration (B=4, d=256, V=4096) on one thread, median of 20 calls
+        try:
+            import ctypes
+            gomp = ctypes.CDLL("libgomp.so.1")
+            wt = synth.WORKLOADS["tiny"]
+            Ht = synth.workload_H("tiny", B=wt["B"])
+            Wt0 = synth.workload_W("tiny")
+            gomp.omp_set_num_threads(1)
+            ts = []
+            for _ in range(20):
+                t1 = time.perf_counter()
+                oracle.fmms_sample(Ht, Wt0, wt["T"], 0, 0)
+                ts.append(time.perf_counter() - t1)
+            gomp.omp_set_num_threads(cores)
+            ts.sort()
+            result["cpu_baseline"]["tiny_single_thread"] = {
+                "config": f"B={wt['B']} d={wt['d']} V={wt['V']}", "threads": 1, "calls": len(ts),
+                "us_per_step_median": round(ts[len(ts) // 2] * 1e6, 1)}
+        except OSError as e:
+            result["cpu_baseline"]["tiny_single_thread"] = {"error": str(e)}
         log(f"cpu baseline {result['cpu_baseline']}")
 
     fs.fs_destroy(ctx)
