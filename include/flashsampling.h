@@ -72,7 +72,7 @@ typedef struct {
 /* Create a context on `device` for calls with B <= max_B, V <= max_V and
  * top_k <= max_top_k.  Allocates the device workspace once; no later call
  * allocates device memory.  With max_top_k > 0 the workspace holds the fused
- * top-k's candidate lists (min(max_B, 64) rows x 256 tiles x 320 bytes);
+ * top-k's candidate lists (min(max_B, 64) rows x 256 tiles x 40 bytes);
  * with max_top_k > 64 also min(max_B, 64) rows of max_V fp32 scores.
  * *out is set to NULL on failure. */
 int fs_create(fs_ctx** out, int device, int max_B, int64_t max_V, int max_top_k);
@@ -116,8 +116,8 @@ int fs_fmms_tiling(fs_ctx* ctx, int B, int d, int64_t V, int path, int64_t* n_ti
  * path: FS_PATH_AUTO, or force the dot-product or MFMA streaming kernel.
  * top_k: 0 (off), or 1 <= top_k <= max_top_k.  With top_k <= 64 (and not the
  *       dot-product path) the top-k is fused: the streaming pass keeps, per
- *       batch row, vocabulary tile and wave, the 4 best scores it saw and a
- *       bound on the scores it dropped; a second launch per batch chunk
+ *       batch row and vocabulary tile, the 4 best scores it saw and a bound
+ *       on the scores it dropped; a second launch per batch chunk
  *       selects the row's top k from those lists, rescoring a tile from H and
  *       W when its bound reaches the k-th score, and draws the Gumbel-max
  *       among them.  No [B, V] scores reach HBM.  Larger k stores each

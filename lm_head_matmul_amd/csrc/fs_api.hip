@@ -26,7 +26,7 @@ struct fs_ctx {
   float* ws_m;
   float* ws_s;
   void* base;
-  // fused top-k: per (row, tile, wave) candidate lists of up to topk_rows rows
+  // fused top-k: per (row, tile) candidate lists of up to topk_rows rows
   uint64_t* topk_lists;
   // top-k from stored scores (k above kTopkFusedMax, the dot path, and the
   // unfused comparator): fp32 scores of up to topk_rows batch rows,
@@ -321,7 +321,7 @@ int noalloc_setup(int dev, NoAllocDevice& out) {
 }
 
 // Fused top-k (and its nucleus): the streaming pass keeps short candidate
-// lists per (row, tile, wave) instead of the scores, and a merge launch per
+// lists per (row, tile) instead of the scores, and a merge launch per
 // batch chunk selects the top k, cuts the nucleus when top_p < 1, and samples.
 int sample_topk_fused(fs_ctx* ctx, hipStream_t stream, const uint16_t* H, int64_t ldh, const uint16_t* W,
                       int64_t ldw, int B, int d, int64_t V, float temperature, uint64_t seed, uint64_t step,

@@ -7,7 +7,7 @@
 namespace fsk {
 
 // EPI_TOPK: the fused top-k pass -- per lane, a short list of the best scores
-// it saw; per (row, tile, wave) a merged list and a bound on what it dropped
+// it saw; per (row, tile) a merged list and a bound on what it dropped
 // (see fs_stream.h), finished by topk_merge_kernel.
 enum Epilogue { EPI_FLAT = 0, EPI_GROUP = 1, EPI_STORE = 2, EPI_TOPK = 3 };
 
