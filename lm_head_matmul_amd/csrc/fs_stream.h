@@ -147,10 +147,14 @@ struct TileRange {
 };
 
 // Online grouped summaries: true once this tile's group has been published
-// (ready[g] == ready_epoch, read with system-scope acquire loads, so a flag in
-// host memory or one written by another stream's work is seen), false if the
-// wait ran out (then *status is set).  Thread 0 polls, sleeping between reads;
-// the barrier hands its answer, and the acquire's ordering, to the workgroup.
+// (ready[g] == ready_epoch, read with system-scope loads, so a flag in host
+// memory or one written by another stream's work is seen), false if the wait
+// ran out (then *status is set).  Thread 0 polls with relaxed loads, sleeping
+// between reads, and acquires once (a fence after the load that saw the
+// epoch): on this GPU an acquire invalidates the XCD's L2, which a poll loop of
+// acquire loads would do on every read, under the tiles of published groups
+// that are streaming beside it.  The barrier hands the answer, and the
+// acquire's ordering, to the workgroup.
 // [arXiv 2603.15854 abstract: grouped variants for online settings; readus.org
 // FlashSampling summary, "Group Gumbel Max": the groups stream past, each one
 // summarized as it comes]
@@ -161,7 +165,8 @@ __device__ __forceinline__ bool group_published(const StreamParams& p) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     int r = 0;
     for (;;) {
-      if (__hip_atomic_load(p.ready + g, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == p.ready_epoch) {
+      if (__hip_atomic_load(p.ready + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == p.ready_epoch) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");  // system scope
         r = 1;
         break;
       }
