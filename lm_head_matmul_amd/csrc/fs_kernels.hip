@@ -580,6 +580,9 @@ __global__ void __launch_bounds__(kThreads) topk_collect_kernel(const TopkParams
 // Thread t holds tile t's list (n_tiles <= kTopkMergeThreads).
 // ---------------------------------------------------------------------------
 static_assert(kTopkMergeThreads == 256 && kTopkMergeCap % kTopkMergeThreads == 0, "merge geometry");
+// every list entry of every tile fits the gather buffer, so the fallback
+// gather (theta = the k-th tile maximum) needs no bound check
+static_assert(kTopkLane * kTopkMergeThreads <= kTopkMergeCap, "one list per tile fits the gather buffer");
 static_assert(kTopkFusedMax <= 64, "the nucleus cut sorts the kept keys within one wave");
 
 // Wave-wide bitonic sort, descending, of one 64-bit key per lane.
