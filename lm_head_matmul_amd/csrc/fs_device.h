@@ -155,6 +155,22 @@ __device__ __forceinline__ void merge_best(float& v, int32_t& i, float ov, int32
   }
 }
 
+template <int OFF>
+__device__ __forceinline__ void merge_best_xor(float& v, int32_t& i) {
+  merge_best(v, i, lane_xor_f<OFF>(v), (int32_t)lane_xor<OFF>((uint32_t)i));
+}
+
+// Wave-wide maximizer: afterwards every lane holds the wave's best (value,
+// index).  Every lane of the wave must be active.
+__device__ __forceinline__ void wave_best(float& v, int32_t& i) {
+  merge_best_xor<32>(v, i);
+  merge_best_xor<16>(v, i);
+  merge_best_xor<8>(v, i);
+  merge_best_xor<4>(v, i);
+  merge_best_xor<2>(v, i);
+  merge_best_xor<1>(v, i);
+}
+
 // Online log-sum-exp state (running max m, sum of exp(x - m)).
 __device__ __forceinline__ void lse_push(float& m, float& s, float x) {
   if (x == -INFINITY) return;

@@ -51,12 +51,7 @@ __global__ void __launch_bounds__(kThreads) sample_logits_kernel(const SamplePar
         }
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int32_t oi = __shfl_xor(bi, off);
-      merge_best(bv, bi, ov, oi);
-    }
+    wave_best(bv, bi);
     if (lane == 0) {
       p.ws_val[(int64_t)b * p.n_tiles + t] = bv;
       p.ws_idx[(int64_t)b * p.n_tiles + t] = bi;
@@ -216,12 +211,7 @@ __device__ __forceinline__ void topk_boundary_block(const uint32_t (&c)[kTopkPer
 // Workgroup maximizer; the result is valid in thread 0.
 __device__ __forceinline__ void topk_block_best(float& bv, int32_t& bi, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int32_t oi = __shfl_xor(bi, off);
-    merge_best(bv, bi, ov, oi);
-  }
+  wave_best(bv, bi);
   __syncthreads();
   if (lane == 0) {
     sh.red_v[wave] = bv;
@@ -933,12 +923,7 @@ __global__ void __launch_bounds__(kTopkMergeThreads) topk_merge_kernel(const Str
       merge_best(bv, bi, topk_key_score(key) + noise_of(id), id);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int32_t oi = __shfl_xor(bi, off);
-    merge_best(bv, bi, ov, oi);
-  }
+  wave_best(bv, bi);
   if (lane == 0) {
     sh.red_v[wave] = bv;
     sh.red_i[wave] = bi;
