@@ -5,7 +5,7 @@
 
 namespace fsk {
 
-// The streaming launches are instantiated in fs_stream_{flat,group,store}.hip.
+// The streaming launches are instantiated in fs_stream_{flat,group,store,topk}.hip.
 extern template hipError_t launch_stream_epi<EPI_FLAT>(const StreamParams&, const StreamConfig&, hipStream_t);
 extern template hipError_t launch_stream_epi<EPI_GROUP>(const StreamParams&, const StreamConfig&, hipStream_t);
 extern template hipError_t launch_stream_epi<EPI_STORE>(const StreamParams&, const StreamConfig&, hipStream_t);

@@ -7,22 +7,26 @@
 // partition of the vocabulary.  [FlashSampling, arXiv 2603.15854, abstract;
 // readus.org FlashSampling summary, section on the two-stage FMMS kernel]
 //
-// Layout on the device (one persistent workgroup of 8 waves per vocab tile):
-//  * A tile is a contiguous, balanced range of 16-row vocab blocks.  Each round
-//    a wave owns MB blocks (16 * MB rows) and streams their rows of W straight
-//    from HBM into VGPRs in the MFMA operand layout: lane (r, g) = (lane % 16,
-//    lane / 16) reads 128 contiguous bytes of row r per 256-wide k sub-block,
-//    as eight 16-byte loads (k chunks 8g .. 8g + 7).  Eight MFMA k-steps then
-//    consume chunk 8g + j from lane group g at step j; the same k permutation
-//    is used for H, so each MFMA still sums over 32 matching k values.
+// Layout on the device (one persistent workgroup per vocabulary tile, one tile
+// per CU):
+//  * A tile is a contiguous, balanced range of 16-row vocab blocks.  Waves
+//    stream their blocks' rows of W straight from HBM into VGPRs in the MFMA
+//    operand layout: lane (r, g) = (lane % 16, lane / 16) holds row r, and lane
+//    group g the k values its 16-byte loads bring (the lane k-layout); H is
+//    read with the same k permutation, so each MFMA still sums over 32
+//    matching k values.
 //  * H (the small operand) sits in LDS: the whole [B, d] when it fits,
-//    otherwise k-chunks double-buffered across the round, prefetched into
-//    registers one chunk ahead.  Rows are padded by 16 bytes so the B-operand
-//    reads of 16 lanes land in distinct banks.
-//  * Epilogue per round, on the accumulators: scale by 1/T, mask, Philox4x32-10
-//    noise (one call covers the four consecutive vocab ids a lane holds), argmax
-//    update.  Per tile, the winners go to a [B, n_tiles] workspace, which a
-//    second small launch on the same stream reduces over tiles.
+//    otherwise k-chunks copied straight from global memory into LDS buffers
+//    (LDS-direct loads) a chunk or two ahead of their use.  Rows are padded by
+//    16 bytes so the B-operand reads of 16 lanes land in distinct banks.
+//  * Up to 64 batch rows: 8 waves per workgroup (the round-major kernel with H
+//    resident, the chunk-outer kernel otherwise); 65 .. 256 rows: the
+//    register-blocked wide kernel, 4 waves.
+//  * Epilogue, on the accumulators: scale by 1/T, mask, Philox4x32-10 noise
+//    (one call covers the four consecutive vocab ids a lane holds), argmax
+//    update (top-k: a short candidate list per lane instead).  Per tile, the
+//    winners go to a [B, n_tiles] workspace, which a second small launch on the
+//    same stream reduces over tiles.
 #pragma once
 
 #include <atomic>
@@ -1477,7 +1481,7 @@ __device__ __forceinline__ void mfma_bf16_asm(bool ag, f32x4_t& acc, const u32x4
 }
 
 // The MFMAs of one k-chunk, group by group (a group: one 32-wide k-step
-// against four batch blocks, for the wave's four vocab block slots), with the
+// against four batch blocks, for the wave's MW vocab block slots), with the
 // vector-memory work of a later chunk spread over the groups: the copies of
 // H chunk c3 into hbuf3, then the W item `it` into dst.  Issued in one burst,
 // those loads held the wave up for as long as the CU's address unit took to
@@ -1541,7 +1545,7 @@ __device__ __forceinline__ void wide_geom(int mb_lo, int mb_hi, int q, int npass
   mb0 = lo + wave * base + (wave < extra ? wave : extra);
 }
 
-// The W item of chunk c of pass q: for block slots m = 0..3, the lane's 16
+// The W item of chunk c of pass q: for block slots m = 0 .. MW - 1, the lane's 16
 // bytes of each of the chunk's k-steps (kouter layout: lane group g feeds k
 // values 8 g .. 8 g + 7 of each 32-wide step).  Slots past the wave's block
 // count repeat its last block (the tile's last with none), so that every item
