@@ -187,11 +187,12 @@ RAGGED = [
     (5, 3072, 3001, 0.8, 0), (16, 2560, 2049, 1.0, 0), (1, 4096, 5000, 1.0, 0),
     # the wide kernel (65 .. 256 rows, d a multiple of 256): eight batch blocks
     # and sixteen, rows past B in the last block, tiles of one vocab block (the
-    # other waves' slots empty), tiles of more than one pass with a partial
-    # last pass, a batch split into 256 rows and a tail of 44 or 1
+    # other waves' slots empty), a batch split into 256 rows and a tail of 44
+    # or 1, and tiles of three and four passes (up to 20 blocks a pass: ~49
+    # and 64 blocks a tile) with a ragged last vocab block
     (65, 512, 999, 1.0, 0), (100, 1024, 777, 0.8, 0), (128, 2048, 4099, 0.7, 0), (129, 512, 1500, 1.0, 0),
     (200, 512, 3001, 0.9, 0), (256, 1024, 9001, 0.8, 0), (136, 512, 70001, 1.0, 0), (300, 512, 2000, 1.0, 0),
-    (257, 512, 1000, 1.1, 0),
+    (257, 512, 1000, 1.1, 0), (136, 256, 200003, 1.0, 0), (256, 256, 262143, 0.9, 0),
     # more than 64 rows with d not a multiple of 256: 64-row chunks
     (129, 264, 1500, 1.0, 0), (70, 520, 999, 1.0, 0),
     # more than 16 rows at d <= 2048: H in chunks although it would fit in LDS
