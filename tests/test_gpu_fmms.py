@@ -192,7 +192,7 @@ RAGGED = [
     # and 64 blocks a tile) with a ragged last vocab block
     (65, 512, 999, 1.0, 0), (100, 1024, 777, 0.8, 0), (128, 2048, 4099, 0.7, 0), (129, 512, 1500, 1.0, 0),
     (200, 512, 3001, 0.9, 0), (256, 1024, 9001, 0.8, 0), (136, 512, 70001, 1.0, 0), (300, 512, 2000, 1.0, 0),
-    (257, 512, 1000, 1.1, 0), (136, 256, 200003, 1.0, 0), (256, 256, 262143, 0.9, 0),
+    (257, 512, 1000, 1.1, 0), (136, 256, 200003, 1.0, 0), (256, 256, 262143, 0.9, 0), (100, 256, 262143, 1.0, 0),
     # more than 64 rows with d not a multiple of 256: 64-row chunks
     (129, 264, 1500, 1.0, 0), (70, 520, 999, 1.0, 0),
     # more than 16 rows at d <= 2048: H in chunks although it would fit in LDS
