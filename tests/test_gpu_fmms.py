@@ -477,10 +477,12 @@ def test_group_summaries_match_group_by_group_calls(fs, ctx):
     assert diff.mean() <= 1e-3 + 1e-9 or np.all(np.abs(a[1][diff] - b[1][diff]) < 1e-3 * (1 + np.abs(b[1][diff])))
 
 
-@pytest.mark.parametrize("B,d,V", [(100, 512, 3001), (128, 1024, 5000), (200, 512, 3001), (256, 512, 70001)])
+@pytest.mark.parametrize("B,d,V", [(100, 512, 3001), (128, 1024, 5000), (200, 512, 3001), (256, 512, 70001),
+                                   (100, 256, 262143), (256, 256, 262143)])
 def test_tile_maxima_wide(fs, ctx, B, d, V):
     # per-tile maximizers of the wide kernel (eight and sixteen batch blocks,
-    # tiles of one pass and of several) against the oracle's
+    # tiles of one pass and of four: 64 blocks a tile at V = 262143) against
+    # the oracle's
     import torch
 
     H = synth.normal_bf16(B, d, seed=300 + B)
